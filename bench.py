@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefill sparse-MoE layer on one MI355X.
+
+One step = the whole layer over one prompt of synthetic tokens already resident
+in HBM: routing (router logits, top-k, histogram, scan, scatter, block map),
+the grouped gate/up + SwiGLU GEMM, the grouped down GEMM and the weighted
+combine, chunk by chunk.  The step enqueues the library's four entry points
+(the same kernels moe_layer_forward enqueues) so HIP events on the launch
+stream can time each kernel inside the timed region.
+
+Prints one JSON line; see --help for options.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE prefill layer tokens/s at 4K tokens; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source; otherwise None."""
+    p = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        tab = json.load(f)
+    ent = tab.get(f"{kernel}@{workload}")
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "q4_grouped_expert_amd", "csrc", ent["source"])
+    if not os.path.exists(src) or source_digest(src) != ent["source_sha256_16"]:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill4096",
+                    help="prefill4096 (default), prefill512, skew2048, long16384 or tiny")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this layer is built and measured on one GPU; multi-GPU runs are not "
+                                   "part of it (token chunks shard with no exchange, experts would need an "
+                                   "all-to-all); run with --gpus 1"}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from q4_grouped_expert_amd import binding as B
+    from q4_grouped_expert_amd import inputs as gen
+    from q4_grouped_expert_amd.device import DeviceLayer
+
+    if args.workload not in gen.WORKLOADS:
+        print(f"unknown workload {args.workload}", file=sys.stderr)
+        return 2
+    shape = gen.WORKLOADS[args.workload]
+    B.lib()  # raises if the HIP library is missing
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = gen.make_layer(shape)
+    dl = DeviceLayer(inp, dev)
+    T, H, I, E, K = shape.T, shape.H, shape.I, shape.E, shape.K
+    chunk = dl.chunk
+    chunks = [(c0, min(T, c0 + chunk)) for c0 in range(0, T, chunk)]
+    rows_max = chunk * K + (chunk if dl.has_shared else 0)
+    route = dl.new_route(chunk)
+    rdesc = B.route_desc(route)
+    h = torch.empty((rows_max, I), dtype=torch.int16, device=dev)
+    y = torch.empty((rows_max, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sgu = dl.s_gate_up.desc if dl.has_shared else None
+    sdn = dl.s_down.desc if dl.has_shared else None
+
+    def step(events=None):
+        for ci, (c0, c1) in enumerate(chunks):
+            d = dl.desc(c1 - c0)
+            ev = events[ci] if events is not None else None
+            if ev: ev[0].record(stream)
+            B.moe_route(d, dl.x[c0:c1], dl.w_router, dl.router_bias, rdesc, None, 0, stream)
+            if ev: ev[1].record(stream)
+            B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], dl.gate_up.desc, sgu, rdesc, h, stream)
+            if ev: ev[2].record(stream)
+            B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h, dl.down.desc, sdn, rdesc, y, stream)
+            if ev: ev[3].record(stream)
+            B.moe_combine(d, y, rdesc, out[c0:c1], stream)
+            if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite layer output"
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in chunks] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = ["route", "gemm_gate_up", "gemm_down", "combine"]
+    per = {n: [] for n in names}
+    for s in range(args.steps):
+        for ev in evs[s]:
+            for i, n in enumerate(names):
+                per[n].append(ev[i].elapsed_time(ev[i + 1]))
+    kernels_ms = {n: float(np.mean(v)) for n, v in per.items()}
+
+    # algorithmic work of the dominant kernel (gate/up GEMM) per launch
+    counts_last = route["counts"].cpu().numpy()
+    rows_per_launch = [(c1 - c0) * K + ((c1 - c0) if dl.has_shared else 0) for c0, c1 in chunks]
+    flop_gu = float(np.mean([2.0 * r * H * 2 * I for r in rows_per_launch]))
+    gu_ms = kernels_ms["gemm_gate_up"]
+    achieved_tflops = flop_gu / (gu_ms * 1e-3) / 1e12
+    flop_dn = float(np.mean([2.0 * r * I * H for r in rows_per_launch]))
+    traffic = load_traffic("gemm_gate_up", args.workload)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+    total_flop = flop_gu * len(chunks) + flop_dn * len(chunks)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: T={T} H={H} I={I} E={E} top-{K}"
+                        f"{' + 1 shared' if dl.has_shared else ''}, SwiGLU, Q4 groupwise-affine g=64 "
+                        f"(bf16 scale+bias), chunk={chunk}"
+                        + (f", Zipf({shape.zipf_s}) router bias" if shape.zipf_s else ""),
+            "tokens": T, "chunk": chunk, "seed": shape.seed, "norm_topk": 1,
+        },
+        "roofline": {
+            "kernel": "gemm_q4_kernel<gate_up+SwiGLU>",
+            "bound": "mfma",
+            "achieved": round(achieved_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "flop_per_launch": flop_gu,
+            "avg_launch_ms": round(gu_ms, 4),
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in kernels_ms.items()},
+        "layer_gemm_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "workspace_bytes_layer_forward": dl.ws_bytes,
+        "nonempty_experts_last_chunk": int((counts_last > 0).sum()),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        S = min(args.cpu_sample_tokens, T)
+        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS") or 16))
+        xs = np.ascontiguousarray(inp.x[:S])
+        t1 = time.perf_counter()
+        oracle.layer_forward(inp, x=xs, nthreads=nthreads)
+        dt = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+                               "sample": f"first {S} of the {T} tokens, whole layer (routing, dequant of every "
+                                         f"expert with rows, SwiGLU FFN, combine), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+"""Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream, every step of the layer runs in the library's HIP kernels.  There is
+no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoeq4.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED_SHAPE = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_MISALIGNED = 4
+MOE_ERR_HIP = 5
+MOE_GEMM_GATE_UP_SWIGLU = 0
+MOE_GEMM_DOWN = 1
+MOE_MAX_EXPERTS = 256
+MOE_MAX_TOPK = 16
+
+# Every function the header declares, with its ctypes signature.
+c_p = ctypes.c_void_p
+
+
+class Q4Desc(ctypes.Structure):
+    _fields_ = [("codes", c_p), ("scales", c_p), ("biases", c_p),
+                ("n_exp", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("has_shared", ctypes.c_int32)]
+
+
+class RouteOutDesc(ctypes.Structure):
+    _fields_ = [("topk_ids", c_p), ("topk_w", c_p), ("counts", c_p), ("offsets", c_p),
+                ("sorted_idx", c_p), ("inv_pos", c_p), ("block_map", c_p), ("n_tiles", c_p)]
+
+
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route_block_rows": (ctypes.c_int, []),
+    "moe_route_max_tiles": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_int32)]),
+    "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(RouteOutDesc),
+                                 c_p, ctypes.c_size_t, c_p]),
+    "moe_grouped_gemm_q4": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, c_p, ctypes.POINTER(Q4Desc),
+                                           ctypes.POINTER(Q4Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p]),
+    "moe_combine": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, ctypes.POINTER(RouteOutDesc), c_p, c_p]),
+    "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
+                                         ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
+                                         c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status}: {status_string(status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (python -m q4_grouped_expert_amd.build); "
+                               "the MoE layer has no other implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _chk(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+# ------------------------------------------------------------------ descriptors
+
+def layer_desc(T, H, I, E, top_k, norm_topk=1, has_shared=1) -> LayerDesc:
+    return LayerDesc(T, H, I, E, top_k, int(norm_topk), int(has_shared))
+
+
+def q4_desc(codes, scales, biases, n_exp, N, K) -> Q4Desc:
+    return Q4Desc(_ptr(codes), _ptr(scales), _ptr(biases), n_exp, N, K)
+
+
+def route_desc(r: dict) -> RouteOutDesc:
+    return RouteOutDesc(*[_ptr(r[k]) for k in ("ids", "w", "counts", "offsets", "sorted_idx", "inv_pos",
+                                                 "block_map", "n_tiles")])
+
+
+# ------------------------------------------------------------------ entry points
+
+def moe_route_block_rows() -> int:
+    return lib().moe_route_block_rows()
+
+
+def moe_route_max_tiles(desc: LayerDesc) -> int:
+    n = ctypes.c_int32()
+    _chk("moe_route_max_tiles", lib().moe_route_max_tiles(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def moe_workspace_size(desc: LayerDesc, kind: int) -> int:
+    n = ctypes.c_size_t()
+    _chk("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(desc), kind, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route(desc, x, w_router, router_bias, route: RouteOutDesc, ws=None, ws_bytes=0, stream=None):
+    _chk("moe_route", lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                      ctypes.byref(route), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_grouped_gemm_q4(desc, mode, a, w: Q4Desc, w_shared: Optional[Q4Desc], route: RouteOutDesc, c,
+                        stream=None):
+    _chk("moe_grouped_gemm_q4", lib().moe_grouped_gemm_q4(
+        ctypes.byref(desc), mode, _ptr(a), ctypes.byref(w),
+        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _stream(stream)))
+
+
+def moe_combine(desc, y, route: RouteOutDesc, out, stream=None):
+    _chk("moe_combine", lib().moe_combine(ctypes.byref(desc), _ptr(y), ctypes.byref(route), _ptr(out),
+                                          _stream(stream)))
+
+
+def moe_layer_forward(desc, x, w_router, router_bias, w_gate_up: Q4Desc, w_down: Q4Desc,
+                      shared_gate_up: Optional[Q4Desc], shared_down: Optional[Q4Desc], out,
+                      route: Optional[RouteOutDesc], ws, ws_bytes, stream=None):
+    byref = lambda d: ctypes.byref(d) if d is not None else None  # noqa: E731
+    _chk("moe_layer_forward", lib().moe_layer_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), byref(w_gate_up), byref(w_down),
+        byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes,
+        _stream(stream)))

@@ -1,0 +1,273 @@
+// Host side of libmoeq4: argument checks, workspace layout and launches.
+// Every check runs before the first HIP call, so a machine without a GPU
+// sees the same status codes.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+using namespace moeq4;
+
+namespace {
+
+constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARGUMENT;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->top_k <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((d->norm_topk != 0 && d->norm_topk != 1) || (d->has_shared != 0 && d->has_shared != 1))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (d->H % MOE_GROUP_SIZE || d->I % MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->E) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // row indices (T*(top_k+1)) stay well inside int32
+  if ((int64_t)d->T * (d->top_k + 1) > (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+int64_t max_tiles_of(const moe_layer_desc* d) {
+  const int64_t R = (int64_t)d->T * d->top_k;
+  const int64_t bm = kTileRows;
+  int64_t n = R / bm + (R < d->E ? R : d->E);
+  if (d->has_shared) n += (d->T + bm - 1) / bm;
+  return n;
+}
+
+struct Layout {
+  size_t ids, w, counts, offsets, sorted, inv, bmap, ntiles, route_end;
+  size_t h, y, total;
+};
+
+Layout layout_of(const moe_layer_desc* d) {
+  const size_t R = (size_t)d->T * d->top_k;
+  const size_t rows = R + (d->has_shared ? (size_t)d->T : 0);
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kAlign);
+    return at;
+  };
+  L.ids = take(R * 4);
+  L.w = take(R * 4);
+  L.counts = take((size_t)d->E * 4);
+  L.offsets = take((size_t)(d->E + 1) * 4);
+  L.sorted = take(R * 4);
+  L.inv = take(R * 4);
+  L.bmap = take((size_t)max_tiles_of(d) * 16);
+  L.ntiles = take(4);
+  L.route_end = o;
+  L.h = take(rows * (size_t)d->I * 2);
+  L.y = take(rows * (size_t)d->H * 4);
+  L.total = o;
+  return L;
+}
+
+int check_q4(const moe_q4_tensor* t, int n_exp, int N, int K) {
+  if (!t || !t->codes || !t->scales || !t->biases) return MOE_ERR_INVALID_ARGUMENT;
+  if (t->n_exp != n_exp || t->N != N || t->K != K) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (misaligned(t->codes) || misaligned(t->scales) || misaligned(t->biases)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+int check_route_out(const moe_route_out* r) {
+  if (!r || !r->topk_ids || !r->topk_w || !r->counts || !r->offsets || !r->sorted_idx || !r->inv_pos ||
+      !r->block_map || !r->n_tiles)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (misaligned(r->topk_ids) || misaligned(r->topk_w) || misaligned(r->counts) || misaligned(r->offsets) ||
+      misaligned(r->sorted_idx) || misaligned(r->inv_pos) || misaligned(r->block_map) || misaligned(r->n_tiles))
+    return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, const float* rb,
+             const moe_route_out* out, hipStream_t s) {
+  RouteArgs a;
+  a.x = x;
+  a.w_router = wr;
+  a.router_bias = rb;
+  a.T = d->T;
+  a.H = d->H;
+  a.E = d->E;
+  a.K = d->top_k;
+  a.norm_topk = d->norm_topk;
+  a.has_shared = d->has_shared;
+  a.out = *out;
+  return hip_status(launch_route(a, s));
+}
+
+int do_gemm(const moe_layer_desc* d, int mode, const void* a, const moe_q4_tensor* w, const moe_q4_tensor* ws,
+            const moe_route_out* r, void* c, hipStream_t s) {
+  GemmArgs g;
+  g.a = reinterpret_cast<const uint16_t*>(a);
+  g.codes = w->codes;
+  g.scales = w->scales;
+  g.biases = w->biases;
+  g.s_codes = ws ? ws->codes : nullptr;
+  g.s_scales = ws ? ws->scales : nullptr;
+  g.s_biases = ws ? ws->biases : nullptr;
+  g.sorted_idx = r->sorted_idx;
+  g.block_map = r->block_map;
+  g.n_tiles = r->n_tiles;
+  g.c = c;
+  g.T = d->T;
+  g.E = d->E;
+  g.topk = d->top_k;
+  g.R = d->T * d->top_k;
+  g.I = d->I;
+  g.max_tiles = (int)max_tiles_of(d);
+  if (mode == MOE_GEMM_GATE_UP_SWIGLU) {
+    g.N = 2 * d->I;
+    g.Kdim = d->H;
+    return hip_status(launch_gemm_gate_up(g, s));
+  }
+  g.N = d->H;
+  g.Kdim = d->I;
+  return hip_status(launch_gemm_down(g, s));
+}
+
+int do_combine(const moe_layer_desc* d, const float* y, const moe_route_out* r, float* out, hipStream_t s) {
+  CombineArgs c;
+  c.y = y;
+  c.topk_w = r->topk_w;
+  c.inv_pos = r->inv_pos;
+  c.out = out;
+  c.T = d->T;
+  c.H = d->H;
+  c.K = d->top_k;
+  c.R = d->T * d->top_k;
+  c.has_shared = d->has_shared;
+  return hip_status(launch_combine(c, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT: a required pointer is NULL or a size is invalid";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE: shape outside what the kernels support";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: device tensors must be 16-byte aligned";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_route_block_rows(void) { return kTileRows; }
+
+int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!max_tiles) return MOE_ERR_INVALID_ARGUMENT;
+  *max_tiles = (int32_t)max_tiles_of(desc);
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes || (ws_kind != 0 && ws_kind != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = ws_kind == 0 ? 0 : layout_of(desc).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+              const moe_route_out* out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;  // the routing kernels keep their scratch in LDS
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if ((rc = check_route_out(out))) return rc;
+  if (misaligned(x) || misaligned(w_router) || (router_bias && misaligned(router_bias))) return MOE_ERR_MISALIGNED;
+  return do_route(desc, x, w_router, router_bias, out, reinterpret_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, const moe_q4_tensor* w,
+                        const moe_q4_tensor* w_shared, const moe_route_out* route, void* c, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (mode != MOE_GEMM_GATE_UP_SWIGLU && mode != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
+  if (desc->T == 0) return MOE_OK;
+  if (!a || !c || !route || !route->sorted_idx || !route->block_map || !route->n_tiles)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int N = mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 * desc->I : desc->H;
+  const int K = mode == MOE_GEMM_GATE_UP_SWIGLU ? desc->H : desc->I;
+  if ((rc = check_q4(w, desc->E, N, K))) return rc;
+  if (desc->has_shared) {
+    if ((rc = check_q4(w_shared, 1, N, K))) return rc;
+  } else {
+    w_shared = nullptr;
+  }
+  if (misaligned(a) || misaligned(c) || misaligned(route->sorted_idx) || misaligned(route->block_map) ||
+      misaligned(route->n_tiles))
+    return MOE_ERR_MISALIGNED;
+  return do_gemm(desc, mode, a, w, w_shared, route, c, reinterpret_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_layer_desc* desc, const float* y, const moe_route_out* route, float* out, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!y || !out || !route || !route->topk_w || !route->inv_pos) return MOE_ERR_INVALID_ARGUMENT;
+  if (misaligned(y) || misaligned(out) || misaligned(route->topk_w) || misaligned(route->inv_pos))
+    return MOE_ERR_MISALIGNED;
+  return do_combine(desc, y, route, out, reinterpret_cast<hipStream_t>(stream));
+}
+
+int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
+                      const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
+                      const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
+                      const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !w_router || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if ((rc = check_q4(w_gate_up, desc->E, 2 * desc->I, desc->H))) return rc;
+  if ((rc = check_q4(w_down, desc->E, desc->H, desc->I))) return rc;
+  if (desc->has_shared) {
+    if ((rc = check_q4(shared_gate_up, 1, 2 * desc->I, desc->H))) return rc;
+    if ((rc = check_q4(shared_down, 1, desc->H, desc->I))) return rc;
+  } else {
+    shared_gate_up = shared_down = nullptr;
+  }
+  if (route_or_null && (rc = check_route_out(route_or_null))) return rc;
+  if (misaligned(x) || misaligned(w_router) || misaligned(out) || misaligned(ws) ||
+      (router_bias && misaligned(router_bias)))
+    return MOE_ERR_MISALIGNED;
+  const Layout L = layout_of(desc);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* base = reinterpret_cast<char*>(ws);
+  moe_route_out r;
+  if (route_or_null) {
+    r = *route_or_null;
+  } else {
+    r.topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
+    r.topk_w = reinterpret_cast<float*>(base + L.w);
+    r.counts = reinterpret_cast<int32_t*>(base + L.counts);
+    r.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    r.sorted_idx = reinterpret_cast<int32_t*>(base + L.sorted);
+    r.inv_pos = reinterpret_cast<int32_t*>(base + L.inv);
+    r.block_map = reinterpret_cast<int32_t*>(base + L.bmap);
+    r.n_tiles = reinterpret_cast<int32_t*>(base + L.ntiles);
+  }
+  void* h = base + L.h;
+  float* y = reinterpret_cast<float*>(base + L.y);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((rc = do_route(desc, x, w_router, router_bias, &r, s))) return rc;
+  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, w_gate_up, shared_gate_up, &r, h, s))) return rc;
+  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, w_down, shared_down, &r, y, s))) return rc;
+  return do_combine(desc, y, &r, out, s);
+}
+
+}  // extern "C"

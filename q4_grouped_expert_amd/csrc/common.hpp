@@ -1,0 +1,84 @@
+// Shared device-side helpers of libmoeq4 (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_q4.h"
+
+namespace moeq4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Rows per GEMM tile in the block map.
+constexpr int kTileRows = 128;
+// Tokens per router workgroup (4 waves x 4 tokens).
+constexpr int kRouteTokens = 16;
+// Hidden-axis chunk staged through LDS by the router.
+constexpr int kRouteChunk = 32;
+// Tokens per scatter pass of the single-workgroup grouping kernel.
+constexpr int kGroupThreads = 1024;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Pack two fp32 values into two bf16 (round to nearest even) in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Device-side launchers (defined in the .hip files, called by api.hip).
+struct RouteArgs {
+  const uint16_t* x;
+  const uint16_t* w_router;
+  const float* router_bias;
+  int T, H, E, K, norm_topk, has_shared;
+  moe_route_out out;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+  const uint16_t* a;        // activations, bf16 [*, Kdim]
+  const uint8_t* codes;     // routed experts [E][N][Kdim/2]
+  const uint16_t* scales;   // [E][N][Kdim/64]
+  const uint16_t* biases;
+  const uint8_t* s_codes;   // shared expert [N][Kdim/2] (or null)
+  const uint16_t* s_scales;
+  const uint16_t* s_biases;
+  const int32_t* sorted_idx;
+  const int32_t* block_map;
+  const int32_t* n_tiles;
+  void* c;                  // output
+  int T, E, topk, R;
+  int N, Kdim;              // weight matrix [N][Kdim]
+  int I;                    // gate/up: intermediate size (h width)
+  int max_tiles;
+};
+hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
+
+struct CombineArgs {
+  const float* y;
+  const float* topk_w;
+  const int32_t* inv_pos;
+  float* out;
+  int T, H, K, R, has_shared;
+};
+hipError_t launch_combine(const CombineArgs& c, hipStream_t stream);
+
+}  // namespace moeq4

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/moe_q4.h declares, and every status code that the
+argument checks can return comes back before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from q4_grouped_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+MIS = 0x10008
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 8
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B.SIGNATURES, n
+
+
+def test_status_strings():
+    for s in range(6):
+        assert B.status_string(s).startswith("MOE_")
+    assert "unknown" in B.status_string(99)
+
+
+def q4(n, N, K, codes=A, scales=A, biases=A):
+    return B.Q4Desc(codes, scales, biases, n, N, K)
+
+
+def full_call(desc, x=A, wr=A, rb=None, gu=None, dn=None, sgu=None, sdn=None, out=A, route=None, ws=A,
+              ws_bytes=None):
+    d = desc
+    gu = gu or q4(d.E, 2 * d.I, d.H)
+    dn = dn or q4(d.E, d.H, d.I)
+    sgu = sgu or q4(1, 2 * d.I, d.H)
+    sdn = sdn or q4(1, d.H, d.I)
+    if ws_bytes is None:
+        ws_bytes = B.moe_workspace_size(d, 1) if B.lib() and d.H > 0 and d.E > 0 else 0
+    return B.lib().moe_layer_forward(ctypes.byref(d), x, wr, rb, ctypes.byref(gu), ctypes.byref(dn),
+                                     ctypes.byref(sgu), ctypes.byref(sdn), out,
+                                     ctypes.byref(route) if route is not None else None, ws, ws_bytes, None)
+
+
+def test_descriptor_validation():
+    L = B.lib()
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(None, 1, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    cases = [
+        (B.layer_desc(-1, 256, 128, 16, 4), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 0, 128, 16, 4), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 256, 128, 16, 0), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 256, 128, 16, 4, norm_topk=2), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 250, 128, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 100, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 128, 16, 17), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 128, 4, 5), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 128, 257, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(1 << 27, 256, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),
+    ]
+    for d, want in cases:
+        assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == want
+        assert full_call(d, ws_bytes=1 << 40) == want
+    d = B.layer_desc(8, 256, 128, 16, 4)
+    assert L.moe_workspace_size(ctypes.byref(d), 2, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_zero_tokens_is_a_noop_before_any_pointer_check():
+    d = B.layer_desc(0, 256, 128, 16, 4)
+    L = B.lib()
+    assert L.moe_layer_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 0,
+                               None) == B.MOE_OK
+    assert L.moe_route(ctypes.byref(d), None, None, None, None, None, 0, None) == B.MOE_OK
+    assert L.moe_combine(ctypes.byref(d), None, None, None, None) == B.MOE_OK
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 0, None, None, None, None, None, None) == B.MOE_OK
+
+
+def test_pointer_shape_alignment_and_workspace_errors():
+    d = B.layer_desc(64, 256, 128, 16, 4)
+    need = B.moe_workspace_size(d, 1)
+    assert need > 0
+    assert full_call(d, x=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert full_call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert full_call(d, ws=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert full_call(d, gu=q4(16, 256, 256, codes=None)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert full_call(d, gu=q4(16, 128, 256)) == B.MOE_ERR_UNSUPPORTED_SHAPE      # N must be 2I
+    assert full_call(d, dn=q4(15, 256, 128)) == B.MOE_ERR_UNSUPPORTED_SHAPE      # n_exp must be E
+    assert full_call(d, sgu=q4(2, 256, 256)) == B.MOE_ERR_UNSUPPORTED_SHAPE      # one shared expert
+    assert full_call(d, x=MIS) == B.MOE_ERR_MISALIGNED
+    assert full_call(d, gu=q4(16, 256, 256, scales=MIS)) == B.MOE_ERR_MISALIGNED
+    assert full_call(d, rb=MIS) == B.MOE_ERR_MISALIGNED
+    bad_route = B.RouteOutDesc(A, A, A, A, A, None, A, A)
+    assert full_call(d, route=bad_route) == B.MOE_ERR_INVALID_ARGUMENT
+    assert full_call(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # no shared expert: its tensors are ignored
+    d2 = B.layer_desc(64, 256, 128, 16, 4, has_shared=0)
+    L = B.lib()
+    gu, dn = q4(16, 256, 256), q4(16, 256, 128)
+    assert L.moe_layer_forward(ctypes.byref(d2), A, A, None, ctypes.byref(gu), ctypes.byref(dn), None, None, A,
+                               None, A, B.moe_workspace_size(d2, 1) - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_entry_point_argument_errors():
+    L = B.lib()
+    d = B.layer_desc(64, 256, 128, 16, 4)
+    r = B.RouteOutDesc(A, A, A, A, A, A, A, A)
+    w = q4(16, 256, 256)
+    ws_ = q4(1, 256, 256)
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 7, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r), A,
+                                 None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 0, A, ctypes.byref(w), None, ctypes.byref(r), A,
+                                 None) == B.MOE_ERR_INVALID_ARGUMENT  # shared expert required
+    wd = q4(16, 256, 128)
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 1, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r), A,
+                                 None) == B.MOE_ERR_UNSUPPORTED_SHAPE  # gate/up tensor passed to down
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 1, MIS, ctypes.byref(wd), ctypes.byref(q4(1, 256, 128)),
+                                 ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_combine(ctypes.byref(d), A, ctypes.byref(r), None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(d), MIS, ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_route(ctypes.byref(d), A, None, None, ctypes.byref(r), None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(B.RouteOutDesc(A, A, A, A, A, A, A, MIS)), None, 0,
+                       None) == B.MOE_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("T,E,K,shared", [(64, 16, 4, 1), (4096, 256, 8, 1), (1, 40, 1, 0), (300, 32, 4, 1)])
+def test_max_tiles_bound(T, E, K, shared):
+    d = B.layer_desc(T, 256, 128, E, K, has_shared=shared)
+    BM = B.moe_route_block_rows()
+    R = T * K
+    assert B.moe_route_max_tiles(d) == R // BM + min(E, R) + (math.ceil(T / BM) if shared else 0)
+
+
+def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
+    small = B.moe_workspace_size(B.layer_desc(512, 2048, 512, 256, 8), 1)
+    big = B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 1)
+    rows = 4096 * 9
+    assert big >= rows * 512 * 2 + rows * 2048 * 4
+    assert big > small
+    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == 0

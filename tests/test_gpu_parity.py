@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element on the same seeded inputs.  Routing (ids, counts, offsets,
+permutation, block map) must be bit-exact; layer outputs must satisfy
+max|err| <= 2e-2 max|ref| and sum|err|/sum|ref| <= 5e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from q4_grouped_expert_amd import binding as B
+from q4_grouped_expert_amd import inputs as gen
+from q4_grouped_expert_amd.device import DeviceLayer, alloc_route
+from tests.parity import assert_out_close, assert_route_equal, host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _announce(what):
+    print(f"\n[gpu case] {what}", flush=True)
+
+
+def run_layer(inp, norm_topk=1, chunk=None):
+    """Full layer on the GPU with routing captured per chunk."""
+    dl = DeviceLayer(inp, DEV, chunk=chunk, norm_topk=norm_topk)
+    T = inp.shape.T
+    routes = []
+    for c0 in range(0, T, dl.chunk):
+        routes.append(dl.new_route(min(dl.chunk, T - c0)))
+    out = dl.forward(routes=routes)
+    torch.cuda.synchronize()
+    return dl, host(out), routes
+
+
+def check_full(inp, norm_topk=1, name=""):
+    _announce(f"{name} T={inp.shape.T} H={inp.shape.H} I={inp.shape.I} E={inp.shape.E} K={inp.shape.K}")
+    s = inp.shape
+    dl, out, routes = run_layer(inp, norm_topk)
+    ref = oracle.layer_forward(inp, norm_topk=norm_topk)
+    assert_route_equal(routes[0], ref, s.K, s.E, s.T, B.moe_route_block_rows(), dl.has_shared, oracle.block_map)
+    return assert_out_close(out, ref["out"])
+
+
+SMALL = {
+    "tiny": gen.WORKLOADS["tiny"],
+    "ragged_T300": gen.custom_shape(300, 512, 256, 32, 4, seed=21, name="ragged"),
+    "T1": gen.custom_shape(1, 256, 128, 16, 4, seed=22),
+    "k1": gen.custom_shape(77, 256, 128, 8, 1, seed=23),
+    "k_eq_E": gen.custom_shape(20, 256, 128, 16, 16, seed=24),
+    "H64_I64": gen.custom_shape(50, 64, 64, 8, 2, seed=25),
+    "E40": gen.custom_shape(130, 256, 128, 40, 6, seed=26),
+    "no_shared": gen.custom_shape(90, 256, 192, 16, 4, shared=False, seed=27),
+    "tall_group": gen.custom_shape(700, 128, 64, 4, 2, seed=28),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small_full_parity(name):
+    check_full(gen.make_layer(SMALL[name]), name=name)
+
+
+def test_layer_norm_topk_off():
+    check_full(gen.make_layer(gen.custom_shape(64, 256, 128, 16, 4, seed=29)), norm_topk=0, name="norm0")
+
+
+def test_duplicated_router_rows_tie_to_lower_expert():
+    inp = gen.make_layer(gen.custom_shape(128, 256, 128, 16, 4, seed=30))
+    inp.w_router[5] = inp.w_router[1]
+    inp.w_router[9] = inp.w_router[1]
+    inp.w_router[12] = inp.w_router[3]
+    check_full(inp, name="dup_router_rows")
+
+
+def test_huge_bias_sends_every_token_to_one_expert():
+    inp = gen.make_layer(gen.custom_shape(300, 256, 128, 16, 4, seed=31))
+    inp.router_bias = np.zeros(16, np.float32)
+    inp.router_bias[7] = 100.0
+    check_full(inp, name="huge_bias")
+    r = oracle.route(inp.x, inp.w_router, 4, rb=inp.router_bias)
+    assert r["counts"][7] == 300
+
+
+def test_prefill512_full_parity():
+    check_full(gen.make_layer(gen.WORKLOADS["prefill512"]), name="prefill512")
+
+
+def _sampled_check(inp, dl, out, routes, n_sample=48, full_route_chunks=(0,), seed=0):
+    s = inp.shape
+    T = s.T
+    BM = B.moe_route_block_rows()
+    for ci in full_route_chunks:
+        c0 = ci * dl.chunk
+        c1 = min(T, c0 + dl.chunk)
+        _announce(f"oracle routing of chunk {ci} ({c1 - c0} tokens)")
+        ref = oracle.route(np.ascontiguousarray(inp.x[c0:c1]), inp.w_router, s.K, rb=inp.router_bias)
+        assert_route_equal(routes[ci], ref, s.K, s.E, c1 - c0, BM, dl.has_shared, oracle.block_map)
+    rng = np.random.default_rng(seed)
+    sample = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
+    _announce(f"oracle layer on {len(sample)} sampled tokens")
+    ref = oracle.layer_forward(inp, x=np.ascontiguousarray(inp.x[sample]))
+    return assert_out_close(out[sample], ref["out"])
+
+
+def test_prefill4096_sampled_parity():
+    inp = gen.make_layer(gen.WORKLOADS["prefill4096"])
+    _announce("prefill4096 GPU run")
+    dl, out, routes = run_layer(inp)
+    _sampled_check(inp, dl, out, routes)
+
+
+def test_skew2048_sampled_parity():
+    inp = gen.make_layer(gen.WORKLOADS["skew2048"])
+    _announce("skew2048 GPU run")
+    dl, out, routes = run_layer(inp)
+    counts = host(routes[0]["counts"])
+    assert counts.max() >= 200 and (counts <= 3).sum() >= 50  # uneven groups, many near-empty
+    _sampled_check(inp, dl, out, routes)
+
+
+def test_long16384_chunked_parity():
+    inp = gen.make_layer(gen.WORKLOADS["long16384"])
+    _announce("long16384 GPU run in 4 chunks of 4096")
+    dl, out, routes = run_layer(inp, chunk=4096)
+    assert len(routes) == 4
+    _sampled_check(inp, dl, out, routes, n_sample=64, full_route_chunks=(0, 3))
+
+
+# -------------------------------------------------------------- entry points
+
+def _route_on_gpu(inp, dl):
+    s = inp.shape
+    r = dl.new_route(s.T)
+    B.moe_route(dl.desc(s.T), dl.x, dl.w_router, dl.router_bias, B.route_desc(r))
+    return r
+
+
+def test_entry_points_separately():
+    inp = gen.make_layer(gen.custom_shape(200, 512, 128, 24, 3, seed=32))
+    s = inp.shape
+    _announce("entry points: moe_route / moe_grouped_gemm_q4 / moe_combine")
+    dl = DeviceLayer(inp, DEV)
+    ref = oracle.layer_forward(inp, want_h=True, want_y=True)
+    R = s.T * s.K
+    rows = R + s.T
+    r = _route_on_gpu(inp, dl)
+    torch.cuda.synchronize()
+    assert_route_equal(r, ref, s.K, s.E, s.T, B.moe_route_block_rows(), True, oracle.block_map)
+    rd = B.route_desc(r)
+    d = dl.desc(s.T)
+    # gate/up + SwiGLU from the GPU's routing
+    h = torch.empty((rows, s.I), dtype=torch.int16, device=DEV)
+    B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x, dl.gate_up.desc, dl.s_gate_up.desc, rd, h)
+    torch.cuda.synchronize()
+    h_gpu = gen.bf16_to_f32(host(h))
+    h_ref = gen.bf16_to_f32(ref["h"])
+    assert_out_close(h_gpu, h_ref, what="h")
+    # down GEMM on the oracle's h: only accumulation order differs
+    h_in = torch.from_numpy(ref["h"].view(np.int16)).to(DEV)
+    y = torch.empty((rows, s.H), dtype=torch.float32, device=DEV)
+    B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h_in, dl.down.desc, dl.s_down.desc, rd, y)
+    torch.cuda.synchronize()
+    assert_out_close(host(y), ref["y"], max_rel=1e-4, mean_rel=1e-5, what="y")
+    # combine on the oracle's y and weights
+    y_in = torch.from_numpy(ref["y"]).to(DEV)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device=DEV)
+    B.moe_combine(d, y_in, rd, out)
+    torch.cuda.synchronize()
+    assert_out_close(host(out), ref["out"], max_rel=1e-5, mean_rel=1e-6, what="combine")
+
+
+def test_zero_tokens_launches_nothing():
+    inp = gen.make_layer(gen.WORKLOADS["tiny"])
+    dl = DeviceLayer(inp, DEV)
+    out = torch.full((1, inp.shape.H), 7.0, device=DEV)
+    dl.forward_chunk(dl.x[:0], out[:0])
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
