@@ -104,7 +104,7 @@ def main() -> int:
             d = dl.desc(c1 - c0)
             ev = events[ci] if events is not None else None
             if ev: ev[0].record(stream)
-            B.moe_route(d, dl.x[c0:c1], dl.w_router, dl.router_bias, rdesc, None, 0, stream)
+            B.moe_route(d, dl.x[c0:c1], dl.w_router, dl.router_bias, rdesc, dl.route_ws, dl.route_ws_bytes, stream)
             if ev: ev[1].record(stream)
             B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], dl.gate_up.desc, sgu, rdesc, h, stream)
             if ev: ev[2].record(stream)

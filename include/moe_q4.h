@@ -135,13 +135,16 @@ int moe_route_block_rows(void);
  * floor(R/BM) + min(E, R) + (has_shared ? ceil(T/BM) : 0).  Host-only. */
 int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 
-/* Workspace bytes needed by moe_route (ws_kind = 0) or moe_layer_forward
- * (ws_kind = 1; includes routing buffers, h and y).  Host-only, pure. */
+/* Workspace bytes needed by moe_route (ws_kind = 0: per-workgroup expert
+ * histograms, (ceil(T/16) * E) int32) or moe_layer_forward (ws_kind = 1;
+ * also routing buffers, h and y).  Host-only, pure.  Workspace contents need
+ * no initialization and are overwritten. */
 int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes);
 
 /* Routing, steps histogram -> scan -> scatter -> block map included.
  * x bf16 [T][H], w_router bf16 [E][H], router_bias fp32 [E] or NULL.
- * Writes every field of *out (all required).  ws: moe_workspace_size(.., 0). */
+ * Writes every field of *out (all required; block_map entries past n_tiles
+ * are left unspecified).  ws: moe_workspace_size(.., 0) bytes, required. */
 int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
               const float* router_bias, const moe_route_out* out, void* ws, size_t ws_bytes,
               void* stream);

@@ -143,7 +143,7 @@ def moe_workspace_size(desc: LayerDesc, kind: int) -> int:
     return n.value
 
 
-def moe_route(desc, x, w_router, router_bias, route: RouteOutDesc, ws=None, ws_bytes=0, stream=None):
+def moe_route(desc, x, w_router, router_bias, route: RouteOutDesc, ws, ws_bytes, stream=None):
     _chk("moe_route", lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
                                       ctypes.byref(route), _ptr(ws), ws_bytes, _stream(stream)))
 

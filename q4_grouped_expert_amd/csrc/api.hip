@@ -37,7 +37,7 @@ int64_t max_tiles_of(const moe_layer_desc* d) {
 }
 
 struct Layout {
-  size_t ids, w, counts, offsets, sorted, inv, bmap, ntiles, route_end;
+  size_t hist, ids, w, counts, offsets, sorted, inv, bmap, ntiles, route_end;
   size_t h, y, total;
 };
 
@@ -51,6 +51,7 @@ Layout layout_of(const moe_layer_desc* d) {
     o = round_up(o + bytes, kAlign);
     return at;
   };
+  L.hist = take(route_workspace_bytes(d->T, d->E));
   L.ids = take(R * 4);
   L.w = take(R * 4);
   L.counts = take((size_t)d->E * 4);
@@ -86,7 +87,7 @@ int check_route_out(const moe_route_out* r) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, const float* rb,
-             const moe_route_out* out, hipStream_t s) {
+             const moe_route_out* out, void* ws, hipStream_t s) {
   RouteArgs a;
   a.x = x;
   a.w_router = wr;
@@ -98,7 +99,7 @@ int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, con
   a.norm_topk = d->norm_topk;
   a.has_shared = d->has_shared;
   a.out = *out;
-  return hip_status(launch_route(a, s));
+  return hip_status(launch_route(a, ws, s));
 }
 
 int do_gemm(const moe_layer_desc* d, int mode, const void* a, const moe_q4_tensor* w, const moe_q4_tensor* ws,
@@ -175,21 +176,21 @@ int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!bytes || (ws_kind != 0 && ws_kind != 1)) return MOE_ERR_INVALID_ARGUMENT;
-  *bytes = ws_kind == 0 ? 0 : layout_of(desc).total;
+  *bytes = ws_kind == 0 ? route_workspace_bytes(desc->T, desc->E) : layout_of(desc).total;
   return MOE_OK;
 }
 
 int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
               const moe_route_out* out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;  // the routing kernels keep their scratch in LDS
   int rc = check_desc(desc);
   if (rc) return rc;
   if (desc->T == 0) return MOE_OK;
-  if (!x || !w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !w_router || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if ((rc = check_route_out(out))) return rc;
-  if (misaligned(x) || misaligned(w_router) || (router_bias && misaligned(router_bias))) return MOE_ERR_MISALIGNED;
-  return do_route(desc, x, w_router, router_bias, out, reinterpret_cast<hipStream_t>(stream));
+  if (misaligned(x) || misaligned(w_router) || misaligned(ws) || (router_bias && misaligned(router_bias)))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < route_workspace_bytes(desc->T, desc->E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return do_route(desc, x, w_router, router_bias, out, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, const moe_q4_tensor* w,
@@ -264,7 +265,7 @@ int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint1
   void* h = base + L.h;
   float* y = reinterpret_cast<float*>(base + L.y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((rc = do_route(desc, x, w_router, router_bias, &r, s))) return rc;
+  if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) return rc;
   if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, w_gate_up, shared_gate_up, &r, h, s))) return rc;
   if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, w_down, shared_down, &r, y, s))) return rc;
   return do_combine(desc, y, &r, out, s);

@@ -17,13 +17,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Rows per GEMM tile in the block map.
-constexpr int kTileRows = 128;
+constexpr int kTileRows = 256;
 // Tokens per router workgroup (4 waves x 4 tokens).
 constexpr int kRouteTokens = 16;
 // Hidden-axis chunk staged through LDS by the router.
 constexpr int kRouteChunk = 32;
-// Tokens per scatter pass of the single-workgroup grouping kernel.
-constexpr int kGroupThreads = 1024;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -50,7 +48,9 @@ struct RouteArgs {
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+// Routing scratch (per-workgroup expert histograms) and launcher.
+size_t route_workspace_bytes(int T, int E);
+hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream);
 
 struct GemmArgs {
   const uint16_t* a;        // activations, bf16 [*, Kdim]

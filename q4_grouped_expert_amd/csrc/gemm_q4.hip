@@ -5,24 +5,38 @@
 // "Qwen 구조와 Prefill 경로").
 //
 // gfx950 mapping
-//  * A workgroup = 4 waves computes one block-map tile (<= 128 rows of one
-//    expert group) against a 128-column slice of the expert's weight matrix.
-//    Each wave owns all the tile's rows and 32 weight rows (two 16-column
-//    MFMA subtiles), so every weight of the slice is dequantized by exactly
-//    one lane of the workgroup.
+//  * One workgroup = 8 waves (two per SIMD) computes one block-map tile
+//    (<= 256 rows of one expert group) against a 256-column slice of that
+//    expert's weights (gate/up: 128 gate + the matching 128 up columns).
+//    Each wave owns every row of the tile and 32 weight columns (two
+//    16-column MFMA subtiles), so every weight of the slice is dequantized by
+//    exactly one lane and the accumulators (<= 128 per lane) sit in AGPRs.
+//  * Ping-pong: in every stage waves 0-3 issue their MFMAs first and then
+//    dequantize the next stage's weights, while waves 4-7 (the other wave on
+//    each SIMD) dequantize first and then issue MFMAs, so on each SIMD one
+//    wave's VALU work runs under the other wave's matrix ops.
+//  * The number of live 16-row subtiles (1..16) is a template parameter,
+//    picked once per workgroup: a 130-row group runs a 9-subtile body with
+//    straight-line code and no MFMAs beyond the last partial subtile.
 //  * Activations (x rows gathered through sorted_idx, or h rows) are staged
 //    in LDS as bf16, 64 reduction columns per stage (one quant group),
-//    double-buffered, with a 16-byte-chunk XOR swizzle so the 16 rows a wave
-//    reads per MFMA hit distinct banks.
-//  * Weights go straight from global memory to VGPRs: a lane loads 8 bytes
-//    = 16 codes of one weight row, applies q*scale+bias in fp32 (fma),
-//    rounds to bf16 (v_cvt_pk_bf16_f32) and feeds the result as the B
-//    operand of v_mfma_f32_16x16x32_bf16; accumulation is fp32.
+//    double-buffered, with a 16-byte-chunk XOR swizzle keyed on row/2.
+//  * Weights go from global memory straight to VGPRs through buffer loads
+//    (per-lane row offset in a VGPR, stage offset in an SGPR), two stages
+//    ahead of use: a lane loads 8 bytes = 16 codes of one weight row, forms
+//    q*scale+bias with one fma per weight in fp32, rounds to bf16 and feeds
+//    the result as the B operand of v_mfma_f32_16x16x32_bf16; accumulation
+//    is fp32.
 //  * The reduction index is permuted identically for A and B inside each
 //    64-wide group (lane group g, MFMA step s -> columns 16g+8s..16g+8s+7),
 //    which lets one 8-byte code load serve both MFMA steps.
-//  * Gate/up mode pairs gate row j and up row I+j in the same wave so the
-//    SwiGLU epilogue h = bf16(silu(g)*u) happens in registers.
+//  * Gate/up mode gives each wave gate rows j and up rows I+j for the same
+//    16 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers.
+//  * Block order: tiles are visited largest first (the block map lists the
+//    shared expert's full tiles last, so it is walked backwards) and the
+//    N-slices of one tile get workgroup ids that are equal modulo 8, which
+//    puts them on the same XCD so the tile's activations are shared in
+//    that XCD's L2.
 #include <math.h>
 
 #include "common.hpp"
@@ -31,14 +45,30 @@ namespace moeq4 {
 
 namespace {
 
-constexpr int BM = kTileRows;  // rows per tile
-constexpr int BK = 64;         // reduction columns per stage (= quant group)
-constexpr int MS = BM / 16;    // 16-row MFMA subtiles per tile
+constexpr int BM = kTileRows;    // max rows per tile (256)
+constexpr int BK = 64;           // reduction columns per stage (= quant group)
+constexpr int NWAVES = 8;        // two waves per SIMD
+constexpr int NT = 64 * NWAVES;  // lanes per workgroup
+constexpr int NS = 2;            // 16-column subtiles per wave
+constexpr int WN = 16 * NS;      // columns per wave
+constexpr int BN = NWAVES * WN;  // weight columns per workgroup
+constexpr int kXcds = 8;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset that reads as zero
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+// 8 codes (element 2i in the low nibble of byte i, 2i+1 in the high) ->
+// bf16(fma(q, s, b)) for each, in element order.  The nibble masks are
+// applied in asm so the compiler converts bytes with v_cvt_f32_ubyte{0..3}.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
-  // d holds 8 codes: element 2i in the low nibble of byte i, 2i+1 in the high
-  const uint32_t lo = d & 0x0F0F0F0Fu;
-  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo, hi;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
+  asm("v_lshrrev_b32 %0, 4, %1\n\tv_and_b32 %0, 0x0f0f0f0f, %0" : "=&v"(hi) : "v"(d));
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -49,21 +79,222 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <bool kGateUp>
-__global__ __launch_bounds__(256) void gemm_q4_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+// 16-byte-chunk swizzle of a 128-byte LDS row: conflict-free for the 16 rows
+// an MFMA fragment read touches, whether LDS serves 8 lanes over 32 banks or
+// 16 lanes over 64 banks per cycle.  An involution: swz(r, swz(r, c)) == c.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
-  const int tile = blockIdx.x;
-  if (tile >= *g.n_tiles) return;  // grid is sized from an upper bound
+struct BRegs {
+  u32x2 c[NS];
+  uint32_t s[NS], b[NS];
+};
+
+// Per-workgroup state shared by every subtile-count instantiation.
+struct TileCtx {
+  rsrc_t a_rs, c_rs, s_rs, b_rs;
+  uint32_t c_off[NS];   // byte offset of this lane's code row + 8*lg
+  uint32_t sb_off[NS];  // byte offset of this lane's scale/bias row
+  int nk;               // stages
+  int row0, nrows;
+  int ocol[NS];
+  bool jval[NS];
+};
+
+template <bool kGateUp, int MSUB>
+__device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* A0, uint16_t* A1,
+                                          uint16_t* A2, uint16_t* A3) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const bool ping = wave < NWAVES / 2;  // MFMA-first half of the waves
+  const int Kd = g.Kdim;
+  constexpr int AROWS = MSUB * 16;
+  constexpr int ADMA = (AROWS + 63) / 64;  // 1-KB LDS-DMA writes per wave per stage
+
+  // Activation staging by direct-to-LDS loads: per stage, DMA i of wave w
+  // fills tile rows 8w + 64i .. +7 (1 KB, 16 B per lane).  Lane l lands at
+  // row 8w + 64i + l/8, physical chunk l%8, so it fetches the logical chunk
+  // that the swizzle maps there.  Rows past the group read zeros (the DMAs
+  // past the live subtiles stay inside the 256-row slot and are never read).
+  uint32_t adoff[ADMA];
+#pragma unroll
+  for (int i = 0; i < ADMA; ++i) {
+    const int r = 8 * wave + 64 * i + (lane >> 3);
+    const int c = swz(r, lane & 7);  // swz is an involution
+    adoff[i] = kOob;
+    if (r < t.nrows) {
+      const int p = t.row0 + r;
+      int src;
+      if (kGateUp) src = (p < g.R) ? g.sorted_idx[p] / g.topk : p - g.R;
+      else src = p;
+      adoff[i] = ((uint32_t)src * (uint32_t)Kd + 8u * c) * 2u;
+    }
+  }
+
+  f32x4 acc[MSUB][NS];
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  BRegs bq[4];
+  bf16x8 bf[2][NS][2];
+
+  auto dma_a = [&](uint16_t* slot, int kt) {
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t.a_rs, (__attribute__((address_space(3))) void*)(slot + (8 * wave + 64 * i) * BK),
+                                                 16, adoff[i], kt * BK * 2, 0, 0);
+  };
+  // Wait until this wave's DMA writes into `slot` have landed: a dummy LDS
+  // read of the slot makes the compiler insert the matching vmcnt wait.
+  auto wait_slot = [&](const uint16_t* slot) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + 8 * wave * BK + 2 * lane);
+    asm volatile("" ::"v"(v));
+  };
+  auto load_b = [&](BRegs& q, int kt) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      q.c[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.c_rs, t.c_off[j], kt * 32, 0));
+      q.s[j] = __builtin_amdgcn_raw_buffer_load_b16(t.s_rs, t.sb_off[j], kt * 2, 0);
+      q.b[j] = __builtin_amdgcn_raw_buffer_load_b16(t.b_rs, t.sb_off[j], kt * 2, 0);
+    }
+  };
+  auto dequant = [&](const BRegs& q, bf16x8 (&dst)[NS][2]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float s = bf16_bits_to_f32(q.s[j]), b = bf16_bits_to_f32(q.b[j]);
+      dst[j][0] = dequant8(q.c[j][0], s, b);
+      dst[j][1] = dequant8(q.c[j][1], s, b);
+    }
+  };
+  auto a_frag = [&](const uint16_t* Ab, int m, int st) {
+    const int r = m * 16 + ln;
+    return *reinterpret_cast<const bf16x8*>(&Ab[r * BK + swz(r, 2 * lg + st) * 8]);
+  };
+  auto mfmas = [&](const bf16x8 (&bcur)[NS][2], const uint16_t* Ab) {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+      const bf16x8 a0 = a_frag(Ab, m, 0), a1 = a_frag(Ab, m, 1);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bcur[j][0], acc[m][j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bcur[j][1], acc[m][j], 0, 0, 0);
+    }
+  };
+
+  // Every wave issues the same, unconditional sequence of loads (stage
+  // indices clamped at the end, rows past the group reading zeros), so the
+  // compiler can count outstanding loads exactly and wait only for the ones
+  // a stage needs.
+  const int nk = t.nk;
+  const int last = nk - 1;
+  dma_a(A0, 0);
+  load_b(bq[0], 0);
+  dma_a(A1, min(1, last));
+  load_b(bq[1], min(1, last));
+  dma_a(A2, min(2, last));
+  load_b(bq[2], min(2, last));
+  load_b(bq[3], min(3, last));
+  dequant(bq[0], bf[0]);
+  wait_slot(A0);
+  __builtin_amdgcn_s_barrier();
+
+  // Stage kt (ring slot kt%4): MFMAs on the slot with the B fragments
+  // dequantized during the previous stage, and the dequant of stage kt+1
+  // (order set by the ping/pong half); then DMA stage kt+3 into the slot read
+  // one stage ago, load the codes of stage kt+4 into the register set just
+  // consumed, wait for this wave's DMA of stage kt+1 (issued two stages ago)
+  // and meet at the barrier (a plain s_barrier: a fenced one would drain
+  // every outstanding load).
+  auto stage = [&](int kt, bf16x8 (&bcur)[NS][2], bf16x8 (&bnext)[NS][2], BRegs& qnext, BRegs& qfree,
+                   const uint16_t* Ab, uint16_t* Anext, uint16_t* Afree) {
+    const bool more = kt + 1 < nk;
+    if (ping) {
+      mfmas(bcur, Ab);
+      if (more) dequant(qnext, bnext);
+    } else {
+      if (more) dequant(qnext, bnext);
+      mfmas(bcur, Ab);
+    }
+    dma_a(Afree, min(kt + 3, last));
+    load_b(qfree, min(kt + 4, last));
+    wait_slot(Anext);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    stage(kt, bf[0], bf[1], bq[1], bq[0], A0, A1, A3);
+    if (kt + 1 < nk) stage(kt + 1, bf[1], bf[0], bq[2], bq[1], A1, A2, A0);
+    if (kt + 2 < nk) stage(kt + 2, bf[0], bf[1], bq[3], bq[2], A2, A3, A1);
+    if (kt + 3 < nk) stage(kt + 3, bf[1], bf[0], bq[0], bq[3], A3, A0, A2);
+  }
+
+  // ---- epilogue: MFMA 16x16 output layout, lane holds rows 4*lg+i, column ln
+  if (kGateUp) {
+    uint16_t* h = reinterpret_cast<uint16_t*>(g.c);
+    if (t.jval[0]) {
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m * 16 + 4 * lg + i;
+          if (r < t.nrows) {
+            const float gv = acc[m][0][i], uv = acc[m][1][i];
+            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+            h[(size_t)(t.row0 + r) * g.I + t.ocol[0]] = f32_to_bf16_bits(gv * sig * uv);
+          }
+        }
+      }
+    }
+  } else {
+    float* y = reinterpret_cast<float*>(g.c);
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * 16 + 4 * lg + i;
+        if (r < t.nrows) {
+#pragma unroll
+          for (int j = 0; j < NS; ++j)
+            if (t.jval[j]) y[(size_t)(t.row0 + r) * g.N + t.ocol[j]] = acc[m][j][i];
+        }
+      }
+    }
+  }
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
+  // activation ring: four stages of [256 rows][64] bf16 (separate objects so
+  // the compiler tracks the direct-to-LDS loads of each slot on its own)
+  __shared__ __attribute__((aligned(16))) uint16_t A0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t A1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t A2[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t A3[BM * BK];
+
+  // ---- which tile / column slice -------------------------------------------
+  const int nN = kGateUp ? (g.I + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+  const int b = blockIdx.x;
+  const int grp = b / (kXcds * nN);
+  const int rem = b % (kXcds * nN);
+  const int nb = rem / kXcds;
+  const int lin = grp * kXcds + rem % kXcds;  // tile rank, largest first
+  const int n_tiles = *g.n_tiles;
+  if (lin >= n_tiles) return;
+  const int tile = n_tiles - 1 - lin;
   const int32_t* bmap = g.block_map + 4 * tile;
-  const int e = bmap[0], row0 = bmap[1], nrows = bmap[2];
+  const int e = bmap[0];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int Kd = g.Kdim;
-  const int cpr = Kd / 2;   // code bytes per weight row
-  const int gpr = Kd / 64;  // quant groups per weight row
+  const uint32_t cpr = Kd / 2;   // code bytes per weight row
+  const uint32_t gpr = Kd / 64;  // quant groups per weight row
 
+  TileCtx t;
+  t.row0 = bmap[1];
+  t.nrows = bmap[2];
+  t.nk = Kd / BK;
   const uint8_t* codes;
   const uint16_t* scl;
   const uint16_t* bia;
@@ -76,160 +307,71 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmArgs g) {
     scl = g.s_scales;
     bia = g.s_biases;
   }
+  t.c_rs = make_rsrc(codes, (uint32_t)g.N * cpr);
+  t.s_rs = make_rsrc(scl, (uint32_t)g.N * gpr * 2u);
+  t.b_rs = make_rsrc(bia, (uint32_t)g.N * gpr * 2u);
+  const uint32_t a_rows = kGateUp ? (uint32_t)g.T : (uint32_t)(g.R + g.T);
+  t.a_rs = make_rsrc(g.a, a_rows * (uint32_t)Kd * 2u);
 
-  // This wave's two weight rows (one per 16-column subtile) for column ln.
-  int wrow[2];
-  bool jval[2];
-  int ocol[2];
+  // This lane's weight rows (one per 16-column subtile).  Subtiles past the
+  // matrix edge read row 0 and are never stored.
   if (kGateUp) {
-    const int j0 = blockIdx.y * 64 + wave * 16;
-    wrow[0] = j0 + ln;
-    wrow[1] = g.I + j0 + ln;
-    jval[0] = jval[1] = true;
-    ocol[0] = ocol[1] = j0 + ln;
+    // subtile 0: gate rows hc..hc+15; subtile 1: the matching up rows I + hc..
+    const int hc = nb * (BN / 2) + wave * 16;
+    const bool v = hc < g.I;
+    t.jval[0] = t.jval[1] = v;
+    t.ocol[0] = t.ocol[1] = hc + ln;
+    const uint32_t rg = v ? hc + ln : 0, ru = v ? g.I + hc + ln : 0;
+    t.c_off[0] = rg * cpr + 8u * lg;
+    t.c_off[1] = ru * cpr + 8u * lg;
+    t.sb_off[0] = rg * gpr * 2u;
+    t.sb_off[1] = ru * gpr * 2u;
   } else {
-    const int c0 = blockIdx.y * 128 + wave * 32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      jval[j] = (c0 + 16 * j) < g.N;
-      ocol[j] = c0 + 16 * j + ln;
-      wrow[j] = jval[j] ? ocol[j] : 0;
+    for (int j = 0; j < NS; ++j) {
+      const int c = nb * BN + wave * WN + 16 * j;
+      t.jval[j] = c < g.N;
+      t.ocol[j] = c + ln;
+      const uint32_t r = t.jval[j] ? c + ln : 0;
+      t.c_off[j] = r * cpr + 8u * lg;
+      t.sb_off[j] = r * gpr * 2u;
     }
   }
 
-  // Activation rows this lane stages: chunk q = tid + 256*i -> row q/8, 16-byte chunk q%8.
-  const int ac = tid & 7;
-  const uint16_t* arow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    arow[i] = nullptr;
-    if (r < nrows) {
-      const int p = row0 + r;
-      if (kGateUp) {
-        const int t = (p < g.R) ? g.sorted_idx[p] / g.topk : p - g.R;
-        arow[i] = g.a + (size_t)t * Kd;
-      } else {
-        arow[i] = g.a + (size_t)p * Kd;
-      }
-    }
-  }
-
-  f32x4 acc[MS][2];
-#pragma unroll
-  for (int m = 0; m < MS; ++m)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 areg[4];
-  u32x2 creg[2];
-  uint32_t sreg[2], breg[2];
-
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      areg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (arow[i]) areg[i] = *reinterpret_cast<const u32x4*>(arow[i] + kt * BK + 8 * ac);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int phys = ac ^ (r & 7);
-      *reinterpret_cast<u32x4*>(&As[buf][r * BK + phys * 8]) = areg[i];
-    }
-  };
-  auto load_w = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      creg[j] = *reinterpret_cast<const u32x2*>(codes + (size_t)wrow[j] * cpr + kt * 32 + 8 * lg);
-      sreg[j] = scl[(size_t)wrow[j] * gpr + kt];
-      breg[j] = bia[(size_t)wrow[j] * gpr + kt];
-    }
-  };
-
-  const int nk = Kd / BK;
-  load_a(0);
-  store_a(0);
-  load_w(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    bf16x8 bfrag[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float s = bf16_bits_to_f32(sreg[j]);
-      const float b = bf16_bits_to_f32(breg[j]);
-      bfrag[j][0] = dequant8(creg[j][0], s, b);
-      bfrag[j][1] = dequant8(creg[j][1], s, b);
-    }
-    if (kt + 1 < nk) {
-      load_a(kt + 1);
-      load_w(kt + 1);
-    }
-    const uint16_t* Ab = As[kt & 1];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int m = 0; m < MS; ++m) {
-        if (m * 16 < nrows) {
-          const int r = m * 16 + ln;
-          const int phys = (2 * lg + st) ^ (r & 7);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ab[r * BK + phys * 8]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (jval[j]) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfrag[j][st], acc[m][j], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < nk) store_a((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // Epilogue.  MFMA 16x16 output layout: lane holds rows 4*lg+i, column ln.
-  if (kGateUp) {
-    uint16_t* h = reinterpret_cast<uint16_t*>(g.c);
-#pragma unroll
-    for (int m = 0; m < MS; ++m) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + 4 * lg + i;
-        if (r < nrows) {
-          const float gv = acc[m][0][i], uv = acc[m][1][i];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          h[(size_t)(row0 + r) * g.I + ocol[0]] = f32_to_bf16_bits(hv);
-        }
-      }
-    }
-  } else {
-    float* y = reinterpret_cast<float*>(g.c);
-#pragma unroll
-    for (int m = 0; m < MS; ++m) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + 4 * lg + i;
-        if (r < nrows) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (jval[j]) y[(size_t)(row0 + r) * g.N + ocol[j]] = acc[m][j][i];
-        }
-      }
-    }
+  const int msub = (t.nrows + 15) >> 4;
+  switch (msub) {
+    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, A3); break;
+    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, A3); break;
+    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, A3); break;
+    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, A3); break;
+    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, A3); break;
+    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, A3); break;
+    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, A3); break;
+    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, A2, A3); break;
+    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, A2, A3); break;
+    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, A2, A3); break;
+    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, A2, A3); break;
+    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, A2, A3); break;
+    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, A2, A3); break;
+    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, A2, A3); break;
+    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, A2, A3); break;
+    default: tile_body<kGateUp, 16>(g, t, A0, A1, A2, A3); break;
   }
 }
+
+int grid_blocks(int max_tiles, int nN) { return (max_tiles + kXcds - 1) / kXcds * kXcds * nN; }
 
 }  // namespace
 
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream) {
-  dim3 grid(g.max_tiles, g.I / 64);
-  hipLaunchKernelGGL(gemm_q4_kernel<true>, grid, dim3(256), 0, stream, g);
+  const int nN = (g.I + BN / 2 - 1) / (BN / 2);
+  hipLaunchKernelGGL(gemm_q4_kernel<true>, dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream) {
-  dim3 grid(g.max_tiles, (g.N + 127) / 128);
-  hipLaunchKernelGGL(gemm_q4_kernel<false>, grid, dim3(256), 0, stream, g);
+  const int nN = (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL(gemm_q4_kernel<false>, dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 

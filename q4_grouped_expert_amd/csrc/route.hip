@@ -26,15 +26,19 @@ namespace moeq4 {
 // staged in LDS as fp32, transposed so a lane's 4 experts (or a wave's 4
 // tokens) are one 16-byte LDS read.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a) {
-  __shared__ __attribute__((aligned(16))) float xs[kRouteChunk][kRouteTokens];
-  __shared__ __attribute__((aligned(16))) float ws[kRouteChunk][MOE_MAX_EXPERTS];
+__global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a, int32_t* __restrict__ hist) {
+  __shared__ __attribute__((aligned(16))) float xs[2][kRouteChunk][kRouteTokens];
+  __shared__ __attribute__((aligned(16))) float ws[2][kRouteChunk][MOE_MAX_EXPERTS];
+  __shared__ int bhist[MOE_MAX_EXPERTS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int t0 = blockIdx.x * kRouteTokens;
   const int T = a.T, H = a.H, E = a.E, K = a.K;
+  constexpr int kCh = kRouteChunk / 8;  // 16-byte pieces per row and chunk
+
+  bhist[tid] = 0;
 
   float acc[4][4];
 #pragma unroll
@@ -42,47 +46,65 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-  for (int h0 = 0; h0 < H; h0 += kRouteChunk) {
-    // router weight row e = tid, kRouteChunk bf16 (16 B per 8)
+  // Chunk staging, one chunk ahead: router row e = tid (kCh x 16 B) and, for
+  // lanes < 16*kCh, one 16-byte piece of a token row.
+  u32x4 wreg[kCh];
+  u32x4 xreg = {0u, 0u, 0u, 0u};
+  const int xt = tid / kCh, xc = tid % kCh;
+  const bool xlane = tid < kRouteTokens * kCh && t0 + xt < T;
+  auto load_chunk = [&](int h0) {
     if (tid < E) {
       const u32x4* src = reinterpret_cast<const u32x4*>(a.w_router + (size_t)tid * H + h0);
 #pragma unroll
-      for (int c = 0; c < kRouteChunk / 8; ++c) {
-        u32x4 v = src[c];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ws[c * 8 + 2 * q][tid] = bf16_bits_to_f32(v[q] & 0xFFFFu);
-          ws[c * 8 + 2 * q + 1][tid] = bf16_bits_to_f32(v[q] >> 16);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < kRouteChunk; ++h) ws[h][tid] = 0.0f;
+      for (int c = 0; c < kCh; ++c) wreg[c] = src[c];
     }
-    // tokens: 16 x kRouteChunk bf16, 16 B per lane
-    constexpr int kCh = kRouteChunk / 8;
-    if (tid < kRouteTokens * kCh) {
-      const int tt = tid / kCh, c = tid % kCh;
-      const int t = t0 + tt;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < T) v = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * H + h0 + 8 * c);
+    if (xlane) xreg = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + xt) * H + h0 + 8 * xc);
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        xs[c * 8 + 2 * q][tt] = bf16_bits_to_f32(v[q] & 0xFFFFu);
-        xs[c * 8 + 2 * q + 1][tt] = bf16_bits_to_f32(v[q] >> 16);
+        const uint32_t v = tid < E ? wreg[c][q] : 0u;
+        ws[buf][c * 8 + 2 * q][tid] = bf16_bits_to_f32(v & 0xFFFFu);
+        ws[buf][c * 8 + 2 * q + 1][tid] = bf16_bits_to_f32(v >> 16);
       }
     }
-    __syncthreads();
+    if (tid < kRouteTokens * kCh) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xs[buf][xc * 8 + 2 * q][xt] = bf16_bits_to_f32(xreg[q] & 0xFFFFu);
+        xs[buf][xc * 8 + 2 * q + 1][xt] = bf16_bits_to_f32(xreg[q] >> 16);
+      }
+    }
+  };
+  auto compute = [&](int buf) {
 #pragma unroll 8
     for (int h = 0; h < kRouteChunk; ++h) {
-      const f32x4 xv = *reinterpret_cast<const f32x4*>(&xs[h][4 * wave]);
-      const f32x4 wv = *reinterpret_cast<const f32x4*>(&ws[h][4 * lane]);
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(&xs[buf][h][4 * wave]);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(&ws[buf][h][4 * lane]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
     }
+  };
+
+  const int nch = H / kRouteChunk;
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) load_chunk((c + 1) * kRouteChunk);
+    compute(0);
+    if (c + 1 < nch) store_chunk(1);
     __syncthreads();
+    if (c + 1 < nch) {
+      if (c + 2 < nch) load_chunk((c + 2) * kRouteChunk);
+      compute(1);
+      if (c + 2 < nch) store_chunk(0);
+      __syncthreads();
+    }
   }
 
   float bias[4];
@@ -160,158 +182,157 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a) {
       if (k < K && lane == k) {
         a.out.topk_ids[(size_t)t * K + k] = sel_e[k];
         a.out.topk_w[(size_t)t * K + k] = expf(sel_v[k] - m) / den;
+        atomicAdd(&bhist[sel_e[k]], 1);
       }
     }
   }
+  __syncthreads();
+  // this workgroup's expert histogram (16 tokens)
+  if (tid < E) hist[(size_t)blockIdx.x * E + tid] = bhist[tid];
 }
 
 // ---------------------------------------------------------------------------
-// Grouping: histogram, exclusive scan, block map and a stable scatter, in one
-// workgroup of 1024 lanes.
+// Exclusive scan of the expert histogram and the tile block map.
 //
-// Stability without ordered atomics: tokens are processed in passes of 1024;
-// in a pass every expert gets a 1024-bit LDS mask of the tokens that chose it
-// (a token's experts are distinct, so one bit per token suffices).  The rank
-// of token t inside expert e's group is the popcount of e's mask below t,
-// plus a running cursor carried across passes.
+// hist[b][e] holds router workgroup b's count for expert e; it is rewritten
+// in place into the exclusive prefix over b (the rows of e that earlier
+// workgroups own), counts[e] is the total, offsets the exclusive scan over e
+// and the block map lists each expert's tiles of at most kTileRows rows, then
+// the shared expert's.  One workgroup, one lane per expert.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGroupThreads) void route_group_kernel(const int32_t* __restrict__ ids, int T,
-                                                                    int K, int E, int has_shared,
-                                                                    moe_route_out out) {
-  constexpr int kWords = kGroupThreads / 64;
-  __shared__ int cnt[MOE_MAX_EXPERTS];
-  __shared__ int off[MOE_MAX_EXPERTS + 1];
-  __shared__ int tstart[MOE_MAX_EXPERTS + 1];
-  __shared__ int cursor[MOE_MAX_EXPERTS];
-  __shared__ unsigned long long bits[MOE_MAX_EXPERTS][kWords];
-
-  const int tid = threadIdx.x;
-  const int R = T * K;
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_scan_kernel(int32_t* __restrict__ hist, int nblk, int T,
+                                                                     int K, int E, int has_shared,
+                                                                     moe_route_out out) {
+  __shared__ int wsum[MOE_MAX_EXPERTS / 64][2];
+  const int e = threadIdx.x;
+  const int lane = e & 63, wave = e >> 6;
   constexpr int BM = kTileRows;
 
-  for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
-  __syncthreads();
-  // ids come from the router kernel and are always in [0, E); the clamp only
-  // guarantees in-bounds indexing if that buffer were ever corrupted
-  auto expert_of = [&](int e) { return (unsigned)e < (unsigned)E ? e : 0; };
-  for (int r = tid; r < R; r += kGroupThreads) atomicAdd(&cnt[expert_of(ids[r])], 1);
-  __syncthreads();
-
-  if (tid < 64) {  // wave 0: scans of counts and of tiles per expert, 4 experts per lane
-    int c[4], nt[4];
-    int sc = 0, st = 0;
+  int run = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * tid + j;
-      c[j] = e < E ? cnt[e] : 0;
-      nt[j] = (c[j] + BM - 1) / BM;
-      sc += c[j];
-      st += nt[j];
-    }
-    int isc = sc, ist = st;
+      for (int i = 0; i < 8; ++i) v[i] = hist[(size_t)(b + i) * E + e];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(isc, o);
-      const int w = __shfl_up(ist, o);
-      if (tid >= o) {
-        isc += v;
-        ist += w;
+      for (int i = 0; i < 8; ++i) {
+        hist[(size_t)(b + i) * E + e] = run;
+        run += v[i];
       }
     }
-    int ex = isc - sc, et = ist - st;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * tid + j;
-      if (e < E) {
-        off[e] = ex;
-        tstart[e] = et;
-      }
-      ex += c[j];
-      et += nt[j];
-    }
-    if (tid == 63) {
-      off[E] = isc;
-      tstart[E] = ist;
+    for (; b < nblk; ++b) {
+      const int v = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += v;
     }
   }
+  const int nt = (run + BM - 1) / BM;
+  // block-wide exclusive scans of counts and tile counts
+  int ic = run, it = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int vc = __shfl_up(ic, o), vt = __shfl_up(it, o);
+    if (lane >= o) {
+      ic += vc;
+      it += vt;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave][0] = ic;
+    wsum[wave][1] = it;
+  }
   __syncthreads();
-
-  for (int e = tid; e < E; e += kGroupThreads) {
-    out.counts[e] = cnt[e];
-    out.offsets[e] = off[e];
-    cursor[e] = off[e];
-    const int nt = (cnt[e] + BM - 1) / BM;
+  int bc = 0, bt = 0;
+  for (int w = 0; w < wave; ++w) {
+    bc += wsum[w][0];
+    bt += wsum[w][1];
+  }
+  const int off = bc + ic - run;
+  const int tst = bt + it - nt;
+  if (e < E) {
+    out.counts[e] = run;
+    out.offsets[e] = off;
     for (int i = 0; i < nt; ++i) {
-      int32_t* b = out.block_map + 4 * (tstart[e] + i);
-      b[0] = e;
-      b[1] = off[e] + i * BM;
-      b[2] = min(BM, cnt[e] - i * BM);
-      b[3] = 0;
+      int32_t* bm = out.block_map + 4 * (tst + i);
+      bm[0] = e;
+      bm[1] = off + i * BM;
+      bm[2] = min(BM, run - i * BM);
+      bm[3] = 0;
     }
   }
-  const int nsh = has_shared ? (T + BM - 1) / BM : 0;
-  for (int i = tid; i < nsh; i += kGroupThreads) {
-    int32_t* b = out.block_map + 4 * (tstart[E] + i);
-    b[0] = E;
-    b[1] = R + i * BM;
-    b[2] = min(BM, T - i * BM);
-    b[3] = 0;
-  }
-  if (tid == 0) {
-    out.offsets[E] = off[E];
-    *out.n_tiles = tstart[E] + nsh;
-  }
-  __syncthreads();
-
-  unsigned long long* flat = &bits[0][0];
-  for (int c0 = 0; c0 < T; c0 += kGroupThreads) {
-    for (int i = tid; i < E * kWords; i += kGroupThreads) flat[i] = 0ull;
-    __syncthreads();
-    const int t = c0 + tid;
-    const bool valid = t < T;
-    const int word = tid >> 6;
-    const unsigned long long bit = 1ull << (tid & 63);
-    int my[MOE_MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      my[k] = 0;
-      if (valid && k < K) {
-        my[k] = expert_of(ids[(size_t)t * K + k]);
-        atomicOr(&bits[my[k]][word], bit);
-      }
+  if (e == MOE_MAX_EXPERTS - 1) {
+    // totals over all lanes (lanes >= E contribute 0)
+    const int R = bc + ic;
+    const int tiles = bt + it;
+    const int nsh = has_shared ? (T + BM - 1) / BM : 0;
+    out.offsets[E] = R;
+    *out.n_tiles = tiles + nsh;
+    for (int i = 0; i < nsh; ++i) {
+      int32_t* bm = out.block_map + 4 * (tiles + i);
+      bm[0] = E;
+      bm[1] = R + i * BM;
+      bm[2] = min(BM, T - i * BM);
+      bm[3] = 0;
     }
-    __syncthreads();
-    if (valid) {
-#pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        if (k < K) {
-          const int e = my[k];
-          int rank = __popcll(bits[e][word] & (bit - 1ull));
-          for (int w = 0; w < word; ++w) rank += __popcll(bits[e][w]);
-          const int p = cursor[e] + rank;
-          out.sorted_idx[p] = t * K + k;
-          out.inv_pos[(size_t)t * K + k] = p;
-        }
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kGroupThreads) {
-      int s = 0;
-#pragma unroll
-      for (int w = 0; w < kWords; ++w) s += __popcll(bits[e][w]);
-      cursor[e] += s;
-    }
-    __syncthreads();
   }
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Stable scatter.  Router workgroup b's tokens land at
+//   offsets[e] + (rows of e owned by workgroups < b) + (rank inside b),
+// the rank being the number of earlier tokens of the same 16-token block that
+// chose e (a 16-bit LDS mask per expert; a token's experts are distinct).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ hist, int T, int K, int E,
+                                                           moe_route_out out) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  for (int e = lane; e < E; e += 64) mask[e] = 0u;
+  __syncthreads();
+  const int t = b * kRouteTokens + lane;
+  const bool valid = lane < kRouteTokens && t < T;
+  int my[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    my[k] = 0;
+    if (valid && k < K) {
+      const int e = out.topk_ids[(size_t)t * K + k];
+      my[k] = (unsigned)e < (unsigned)E ? e : 0;  // ids are produced in range; clamp keeps indexing safe
+      atomicOr(&mask[my[k]], 1u << lane);
+    }
+  }
+  __syncthreads();
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      if (k < K) {
+        const int e = my[k];
+        const int rank = __popc(mask[e] & ((1u << lane) - 1u));
+        const int p = out.offsets[e] + hist[(size_t)b * E + e] + rank;
+        out.sorted_idx[p] = t * K + k;
+        out.inv_pos[(size_t)t * K + k] = p;
+      }
+    }
+  }
+}
+
+size_t route_workspace_bytes(int T, int E) {
+  const size_t nb = (size_t)(T + kRouteTokens - 1) / kRouteTokens;
+  return nb * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL(route_logits_topk_kernel, dim3(nb), dim3(256), 0, stream, a);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(route_logits_topk_kernel, dim3(nb), dim3(256), 0, stream, a, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(kGroupThreads), 0, stream, a.out.topk_ids, a.T, a.K,
-                     a.E, a.has_shared, a.out);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, nb, a.T, a.K, a.E,
+                     a.has_shared, a.out);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(64), 0, stream, hist, a.T, a.K, a.E, a.out);
   return hipGetLastError();
 }
 

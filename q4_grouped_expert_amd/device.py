@@ -58,6 +58,8 @@ class DeviceLayer:
         self.ws_bytes = B.moe_workspace_size(d, 1)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.max_tiles = B.moe_route_max_tiles(d)
+        self.route_ws_bytes = B.moe_workspace_size(d, 0)
+        self.route_ws = torch.empty(max(self.route_ws_bytes, 256), dtype=torch.uint8, device=device)
 
     def desc(self, T: int) -> B.LayerDesc:
         s = self.shape

@@ -131,9 +131,13 @@ def test_entry_point_argument_errors():
                                  ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
     assert L.moe_combine(ctypes.byref(d), A, ctypes.byref(r), None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(ctypes.byref(d), MIS, ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
-    assert L.moe_route(ctypes.byref(d), A, None, None, ctypes.byref(r), None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(B.RouteOutDesc(A, A, A, A, A, A, A, MIS)), None, 0,
-                       None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_route(ctypes.byref(d), A, None, None, ctypes.byref(r), A, 1 << 20, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), None, 1 << 20, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(B.RouteOutDesc(A, A, A, A, A, A, A, MIS)), A,
+                       1 << 20, None) == B.MOE_ERR_MISALIGNED
+    need = B.moe_workspace_size(d, 0)
+    assert need == 4 * 16 * 4
+    assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), A, need - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 @pytest.mark.parametrize("T,E,K,shared", [(64, 16, 4, 1), (4096, 256, 8, 1), (1, 40, 1, 0), (300, 32, 4, 1)])
@@ -150,4 +154,4 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     rows = 4096 * 9
     assert big >= rows * 512 * 2 + rows * 2048 * 4
     assert big > small
-    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == 0
+    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == 256 * 256 * 4

@@ -132,7 +132,7 @@ def test_long16384_chunked_parity():
 def _route_on_gpu(inp, dl):
     s = inp.shape
     r = dl.new_route(s.T)
-    B.moe_route(dl.desc(s.T), dl.x, dl.w_router, dl.router_bias, B.route_desc(r))
+    B.moe_route(dl.desc(s.T), dl.x, dl.w_router, dl.router_bias, B.route_desc(r), dl.route_ws, dl.route_ws_bytes)
     return r
 
 
