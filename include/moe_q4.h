@@ -57,8 +57,8 @@ extern "C" {
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1,   /* required pointer NULL, dimension < 0 or == 0 where not allowed */
-  MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H or I not a multiple of 64, top_k > E, top_k or E above maximum,
-                                     tensor shape not matching the descriptor */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H or I not a multiple of 64 or above MOE_MAX_REDUCTION, top_k > E,
+                                     top_k or E above maximum, tensor shape not matching the descriptor */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,
   MOE_ERR_MISALIGNED = 4,         /* a device tensor not 16-byte aligned */
   MOE_ERR_HIP = 5                 /* a kernel launch failed */
@@ -67,6 +67,7 @@ enum moe_status {
 #define MOE_MAX_EXPERTS 256   /* routed experts per layer */
 #define MOE_MAX_TOPK 16       /* experts chosen per token */
 #define MOE_GROUP_SIZE 64     /* weights per (scale, bias) pair */
+#define MOE_MAX_REDUCTION 2048 /* H and I: a GEMM keeps a tile's scales/biases on chip */
 
 /* Groupwise-affine 4-bit weights of n_exp experts, each an [N, K] matrix
  * (N output rows, K reduction columns), stored as

@@ -22,6 +22,7 @@ int check_desc(const moe_layer_desc* d) {
   if ((d->norm_topk != 0 && d->norm_topk != 1) || (d->has_shared != 0 && d->has_shared != 1))
     return MOE_ERR_INVALID_ARGUMENT;
   if (d->H % MOE_GROUP_SIZE || d->I % MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->H > MOE_MAX_REDUCTION || d->I > MOE_MAX_REDUCTION) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->E) return MOE_ERR_UNSUPPORTED_SHAPE;
   // row indices (T*(top_k+1)) stay well inside int32
   if ((int64_t)d->T * (d->top_k + 1) > (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED_SHAPE;

@@ -18,6 +18,8 @@ constexpr int kWave = 64;
 
 // Rows per GEMM tile in the block map.
 constexpr int kTileRows = 256;
+// Quant groups per weight row the GEMM keeps in LDS (reduction dim <= 2048).
+constexpr int kMaxGroupsPerRow = 32;
 // Tokens per router workgroup (4 waves x 4 tokens).
 constexpr int kRouteTokens = 16;
 // Hidden-axis chunk staged through LDS by the router.

@@ -53,6 +53,7 @@ constexpr int NS = 2;            // 16-column subtiles per wave
 constexpr int WN = 16 * NS;      // columns per wave
 constexpr int BN = NWAVES * WN;  // weight columns per workgroup
 constexpr int kXcds = 8;
+constexpr int kMaxGroups = kMaxGroupsPerRow;  // scale/bias groups per weight row kept in LDS
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -86,14 +87,15 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 
 struct BRegs {
   u32x2 c[NS];
-  uint32_t s[NS], b[NS];
 };
 
 // Per-workgroup state shared by every subtile-count instantiation.
 struct TileCtx {
   rsrc_t a_rs, c_rs, s_rs, b_rs;
   uint32_t c_off[NS];   // byte offset of this lane's code row + 8*lg
-  uint32_t sb_off[NS];  // byte offset of this lane's scale/bias row
+  int sb_row[NS];       // this lane's rows in the LDS scale/bias tables
+  uint32_t sb_src[2];   // byte offsets of the (up to two) contiguous row ranges
+  int sb_half;          // 16-byte chunks per range
   int nk;               // stages
   int row0, nrows;
   int ocol[NS];
@@ -102,11 +104,12 @@ struct TileCtx {
 
 template <bool kGateUp, int MSUB>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* A0, uint16_t* A1,
-                                          uint16_t* A2, uint16_t* A3) {
+                                          uint16_t* A2, uint16_t* A3, uint16_t* Ssh, uint16_t* Bsh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const bool ping = wave < NWAVES / 2;  // MFMA-first half of the waves
   const int Kd = g.Kdim;
+  const int gpr = Kd / 64;  // quant groups per weight row
   constexpr int AROWS = MSUB * 16;
   constexpr int ADMA = (AROWS + 63) / 64;  // 1-KB LDS-DMA writes per wave per stage
 
@@ -153,18 +156,39 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   };
   auto load_b = [&](BRegs& q, int kt) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
+    for (int j = 0; j < NS; ++j)
       q.c[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.c_rs, t.c_off[j], kt * 32, 0));
-      q.s[j] = __builtin_amdgcn_raw_buffer_load_b16(t.s_rs, t.sb_off[j], kt * 2, 0);
-      q.b[j] = __builtin_amdgcn_raw_buffer_load_b16(t.b_rs, t.sb_off[j], kt * 2, 0);
-    }
   };
-  auto dequant = [&](const BRegs& q, bf16x8 (&dst)[NS][2]) {
+  // scale and bias of stage kt's quant group, from the tile's LDS tables
+  auto dequant = [&](const BRegs& q, bf16x8 (&dst)[NS][2], int kt) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const float s = bf16_bits_to_f32(q.s[j]), b = bf16_bits_to_f32(q.b[j]);
+      const int idx = t.sb_row[j] * gpr + kt;
+      const float s = bf16_bits_to_f32(Ssh[idx]), b = bf16_bits_to_f32(Bsh[idx]);
       dst[j][0] = dequant8(q.c[j][0], s, b);
       dst[j][1] = dequant8(q.c[j][1], s, b);
+    }
+  };
+  // The tile's scales and biases for the whole reduction: one or two
+  // contiguous row ranges per table, fetched once as whole cache lines with
+  // 16-byte direct-to-LDS loads (chunk q of range r lands at LDS byte
+  // 16*(r*half + q)).  Chunks past a range read zeros into the slack of the
+  // table.
+  auto dma_sb = [&]() {
+    const int chunks = 2 * t.sb_half;  // both ranges
+#pragma unroll
+    for (int round = 0; round < (32 * kMaxGroups + NT - 1) / NT; ++round) {  // <= 32*gpr chunks
+      const int q0 = NT * round + 64 * wave;  // first chunk of this wave's DMA
+      if (q0 < chunks) {
+        const int q = q0 + lane;
+        const int r = q >= t.sb_half;
+        const int qi = q - r * t.sb_half;
+        const uint32_t off = (q < chunks) ? t.sb_src[r] + 16u * qi : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t.s_rs, (__attribute__((address_space(3))) void*)(Ssh + 8 * q0), 16, off,
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t.b_rs, (__attribute__((address_space(3))) void*)(Bsh + 8 * q0), 16, off,
+                                                 0, 0, 0);
+      }
     }
   };
   auto a_frag = [&](const uint16_t* Ab, int m, int st) {
@@ -188,6 +212,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   // a stage needs.
   const int nk = t.nk;
   const int last = nk - 1;
+  dma_sb();
   dma_a(A0, 0);
   load_b(bq[0], 0);
   dma_a(A1, min(1, last));
@@ -195,9 +220,11 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   dma_a(A2, min(2, last));
   load_b(bq[2], min(2, last));
   load_b(bq[3], min(3, last));
-  dequant(bq[0], bf[0]);
+  wait_slot(Ssh);
+  wait_slot(Bsh);
   wait_slot(A0);
   __builtin_amdgcn_s_barrier();
+  dequant(bq[0], bf[0], 0);
 
   // Stage kt (ring slot kt%4): MFMAs on the slot with the B fragments
   // dequantized during the previous stage, and the dequant of stage kt+1
@@ -211,9 +238,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     const bool more = kt + 1 < nk;
     if (ping) {
       mfmas(bcur, Ab);
-      if (more) dequant(qnext, bnext);
+      if (more) dequant(qnext, bnext, kt + 1);
     } else {
-      if (more) dequant(qnext, bnext);
+      if (more) dequant(qnext, bnext, kt + 1);
       mfmas(bcur, Ab);
     }
     dma_a(Afree, min(kt + 3, last));
@@ -271,6 +298,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t A1[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t A2[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t A3[BM * BK];
+  // the tile's scales and biases: [256 weight rows][<= 32 groups] bf16 each
+  __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kMaxGroups];
+  __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kMaxGroups];
 
   // ---- which tile / column slice -------------------------------------------
   const int nN = kGateUp ? (g.I + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
@@ -324,8 +354,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
     const uint32_t rg = v ? hc + ln : 0, ru = v ? g.I + hc + ln : 0;
     t.c_off[0] = rg * cpr + 8u * lg;
     t.c_off[1] = ru * cpr + 8u * lg;
-    t.sb_off[0] = rg * gpr * 2u;
-    t.sb_off[1] = ru * gpr * 2u;
+    // scale/bias tables: rows 0..127 = gate rows nb*128.., 128..255 = up rows
+    t.sb_row[0] = wave * 16 + ln;
+    t.sb_row[1] = BN / 2 + wave * 16 + ln;
+    t.sb_half = (BN / 2) * gpr * 2 / 16;
+    t.sb_src[0] = (uint32_t)(nb * (BN / 2)) * gpr * 2u;
+    t.sb_src[1] = (uint32_t)(g.I + nb * (BN / 2)) * gpr * 2u;
   } else {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -334,28 +368,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
       t.ocol[j] = c + ln;
       const uint32_t r = t.jval[j] ? c + ln : 0;
       t.c_off[j] = r * cpr + 8u * lg;
-      t.sb_off[j] = r * gpr * 2u;
+      t.sb_row[j] = wave * WN + 16 * j + ln;
     }
+    // one contiguous range of 256 rows, split in two halves of 128
+    t.sb_half = (BN / 2) * gpr * 2 / 16;
+    t.sb_src[0] = (uint32_t)(nb * BN) * gpr * 2u;
+    t.sb_src[1] = (uint32_t)(nb * BN + BN / 2) * gpr * 2u;
   }
 
   const int msub = (t.nrows + 15) >> 4;
   switch (msub) {
-    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, A3); break;
-    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, A3); break;
-    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, A3); break;
-    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, A3); break;
-    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, A3); break;
-    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, A3); break;
-    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, A3); break;
-    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, A2, A3); break;
-    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, A2, A3); break;
-    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, A2, A3); break;
-    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, A2, A3); break;
-    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, A2, A3); break;
-    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, A2, A3); break;
-    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, A2, A3); break;
-    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, A2, A3); break;
-    default: tile_body<kGateUp, 16>(g, t, A0, A1, A2, A3); break;
+    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    default: tile_body<kGateUp, 16>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
   }
 }
 

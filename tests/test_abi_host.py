@@ -70,6 +70,8 @@ def test_descriptor_validation():
         (B.layer_desc(8, 256, 128, 16, 17), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(8, 256, 128, 4, 5), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(8, 256, 128, 257, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 4096, 128, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 2112, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(1 << 27, 256, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),
     ]
     for d, want in cases:
