@@ -24,8 +24,11 @@ int check_desc(const moe_layer_desc* d) {
   if (d->H % MOE_GROUP_SIZE || d->I % MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->H > MOE_MAX_REDUCTION || d->I > MOE_MAX_REDUCTION) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->E) return MOE_ERR_UNSUPPORTED_SHAPE;
-  // row indices (T*(top_k+1)) stay well inside int32
+  // row indices (T*(top_k+1)) stay well inside int32, and every activation
+  // tensor the kernels address through 32-bit buffer offsets stays below 2 GiB
   if ((int64_t)d->T * (d->top_k + 1) > (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)d->T * d->H * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)d->T * (d->top_k + 1) * d->I * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
 }
 

@@ -73,6 +73,7 @@ def test_descriptor_validation():
         (B.layer_desc(8, 4096, 128, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(8, 256, 2112, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(1 << 27, 256, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(1 << 20, 2048, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),  # T*H*2 >= 2 GiB
     ]
     for d, want in cases:
         assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == want
@@ -138,7 +139,7 @@ def test_entry_point_argument_errors():
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(B.RouteOutDesc(A, A, A, A, A, A, A, MIS)), A,
                        1 << 20, None) == B.MOE_ERR_MISALIGNED
     need = B.moe_workspace_size(d, 0)
-    assert need == 4 * 16 * 4
+    assert need == 4 * 16 * 4 + 256 * 4
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), A, need - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -156,4 +157,4 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     rows = 4096 * 9
     assert big >= rows * 512 * 2 + rows * 2048 * 4
     assert big > small
-    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == 256 * 256 * 4
+    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == 256 * 256 * 4 + 256 * 4
