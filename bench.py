@@ -52,6 +52,22 @@ def load_traffic(kernel: str, workload: str):
     return ent["hbm_bytes_per_launch"]
 
 
+def copy_calibration(args, torch) -> int:
+    """A plain copy of known size: reads and writes n bytes per launch."""
+    n = args.copy_calibration_mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps, "ms_per_launch": round(dt * 1e3, 4),
+                      "read_plus_write_GBs": round(2 * n / dt / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,7 +76,11 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill4096",
                     help="prefill4096 (default), prefill512, skew2048, long16384 or tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
+                    help="tokens of the workload the CPU oracle is timed on (from the first)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the layer, run a plain device-to-device copy of this many MiB "
+                         "(--steps times); its counter readings scale the HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -77,6 +97,8 @@ def main() -> int:
     from q4_grouped_expert_amd import inputs as gen
     from q4_grouped_expert_amd.device import DeviceLayer
 
+    if args.copy_calibration_mib:
+        return copy_calibration(args, torch)
     if args.workload not in gen.WORKLOADS:
         print(f"unknown workload {args.workload}", file=sys.stderr)
         return 2
@@ -143,6 +165,32 @@ def main() -> int:
     flop_dn = float(np.mean([2.0 * r * I * H for r in rows_per_launch]))
     traffic = load_traffic("gemm_gate_up", args.workload)
 
+    # per-kernel rates over the algorithmic bytes each one must move (per launch = per chunk)
+    n_ne = int((counts_last > 0).sum()) + (1 if dl.has_shared else 0)
+    wb_gu = 2 * I * H // 2 + 2 * I * (H // 64) * 4      # codes + bf16 scale and bias, one expert
+    wb_dn = H * I // 2 + H * (I // 64) * 4
+    rows_m = float(np.mean(rows_per_launch))
+    Tc = float(np.mean([c1 - c0 for c0, c1 in chunks]))
+    Rc = Tc * K
+    route_bytes = Tc * H * 2 + E * H * 2 + Rc * 8 + 2 * Rc * 4 + (2 * E + 1) * 4
+    comb_bytes = rows_m * H * 4 + Tc * H * 4 + Rc * 8
+
+    def rate(b, ms):
+        return round(b / (ms * 1e-3) / 1e9, 1)
+
+    kernels = {
+        "route": {"ms": round(kernels_ms["route"], 4), "GBs": rate(route_bytes, kernels_ms["route"]),
+                  "router_TFLOPs": round(2 * Tc * H * E / (kernels_ms["route"] * 1e-3) / 1e12, 2)},
+        "gemm_gate_up": {"ms": round(gu_ms, 4), "TFLOPs": round(achieved_tflops, 2),
+                         "mfma_frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                         "weight_GBs": rate(n_ne * wb_gu, gu_ms)},
+        "gemm_down": {"ms": round(kernels_ms["gemm_down"], 4),
+                      "TFLOPs": round(flop_dn / (kernels_ms["gemm_down"] * 1e-3) / 1e12, 2),
+                      "mfma_frac": round(flop_dn / (kernels_ms["gemm_down"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "weight_GBs": rate(n_ne * wb_dn, kernels_ms["gemm_down"])},
+        "combine": {"ms": round(kernels_ms["combine"], 4), "GBs": rate(comb_bytes, kernels_ms["combine"])},
+    }
+
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
     total_flop = flop_gu * len(chunks) + flop_dn * len(chunks)
@@ -177,7 +225,7 @@ def main() -> int:
             "flop_per_launch": flop_gu,
             "avg_launch_ms": round(gu_ms, 4),
         },
-        "kernels_ms": {k: round(v, 4) for k, v in kernels_ms.items()},
+        "kernels": kernels,
         "layer_gemm_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "workspace_bytes_layer_forward": dl.ws_bytes,
         "nonempty_experts_last_chunk": int((counts_last > 0).sum()),
