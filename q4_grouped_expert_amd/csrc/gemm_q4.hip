@@ -5,33 +5,36 @@
 // "Qwen 구조와 Prefill 경로").
 //
 // gfx950 mapping
-//  * One workgroup = 8 waves (two per SIMD) computes one block-map tile
-//    (<= 256 rows of one expert group) against a 256-column slice of that
-//    expert's weights (gate/up: 128 gate + the matching 128 up columns).
-//    Each wave owns every row of the tile and 32 weight columns (two
-//    16-column MFMA subtiles), so every weight of the slice is dequantized by
-//    exactly one lane and the accumulators (<= 128 per lane) sit in AGPRs.
-//  * Ping-pong: in every stage waves 0-3 issue their MFMAs first and then
-//    dequantize the next stage's weights, while waves 4-7 (the other wave on
-//    each SIMD) dequantize first and then issue MFMAs, so on each SIMD one
-//    wave's VALU work runs under the other wave's matrix ops.
-//  * The number of live 16-row subtiles (1..16) is a template parameter,
-//    picked once per workgroup: a 130-row group runs a 9-subtile body with
+//  * One workgroup = 4 waves, one per SIMD, and two workgroups share a CU
+//    (80 KB of LDS and at most 256 registers per wave each), so every SIMD
+//    runs two independent waves: while one issues MFMAs the other dequantizes,
+//    waits at its barrier or runs its prologue/epilogue.
+//  * A workgroup computes one block-map tile (<= 128 rows of one expert
+//    group) against a 256-column slice of that expert's weights (gate/up:
+//    128 gate + the matching 128 up columns).  Each wave owns every row of the
+//    tile and 64 weight columns (four 16-column MFMA subtiles): every weight of
+//    the slice is dequantized by exactly one lane, the accumulators (<= 128
+//    per lane) sit in AGPRs, and each activation fragment read from LDS feeds
+//    4 MFMAs.
+//  * The number of live 16-row subtiles (1..8) is a template parameter,
+//    picked once per workgroup: a 70-row group runs a 5-subtile body with
 //    straight-line code and no MFMAs beyond the last partial subtile.
-//  * Activations (x rows gathered through sorted_idx, or h rows) are staged
-//    in LDS as bf16, 64 reduction columns per stage (one quant group),
-//    double-buffered, with a 16-byte-chunk XOR swizzle keyed on row/2.
+//  * Activations (x rows gathered through sorted_idx, or h rows) reach LDS by
+//    direct-to-LDS buffer loads into a 3-slot ring of 64-column stages (one
+//    quant group each), issued two stages ahead of use, with a 16-byte-chunk
+//    XOR swizzle that keeps MFMA fragment reads conflict-free.
 //  * Weights go from global memory straight to VGPRs through buffer loads
-//    (per-lane row offset in a VGPR, stage offset in an SGPR), two stages
+//    (per-lane row offset in a VGPR, stage offset in an SGPR), three stages
 //    ahead of use: a lane loads 8 bytes = 16 codes of one weight row, forms
 //    q*scale+bias with one fma per weight in fp32, rounds to bf16 and feeds
 //    the result as the B operand of v_mfma_f32_16x16x32_bf16; accumulation
-//    is fp32.
+//    is fp32.  The tile's scales and biases for the whole reduction are
+//    loaded once per tile into LDS tables.
 //  * The reduction index is permuted identically for A and B inside each
 //    64-wide group (lane group g, MFMA step s -> columns 16g+8s..16g+8s+7),
 //    which lets one 8-byte code load serve both MFMA steps.
 //  * Gate/up mode gives each wave gate rows j and up rows I+j for the same
-//    16 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers.
+//    32 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers.
 //  * Block order: tiles are visited largest first (the block map lists the
 //    shared expert's full tiles last, so it is walked backwards) and the
 //    N-slices of one tile get workgroup ids that are equal modulo 8, which
@@ -39,17 +42,20 @@
 //    that XCD's L2.
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 
 namespace moeq4 {
 
 namespace {
 
-constexpr int BM = kTileRows;    // max rows per tile (256)
+constexpr int BM = kTileRows;    // max rows per tile (128 = 8 MFMA subtiles)
 constexpr int BK = 64;           // reduction columns per stage (= quant group)
-constexpr int NWAVES = 8;        // two waves per SIMD
+constexpr int NWAVES = 4;        // one wave per SIMD
 constexpr int NT = 64 * NWAVES;  // lanes per workgroup
-constexpr int NS = 2;            // 16-column subtiles per wave
+constexpr int NS = 4;            // 16-column subtiles per wave
 constexpr int WN = 16 * NS;      // columns per wave
 constexpr int BN = NWAVES * WN;  // weight columns per workgroup
 constexpr int kXcds = 8;
@@ -85,6 +91,17 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
 // 16 lanes over 64 banks per cycle.  An involution: swz(r, swz(r, c)) == c.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
+// Accumulate and start-of-tile forms of v_mfma_f32_16x16x32_bf16.  The
+// first reduction step of a tile uses the inline constant 0 as accumulator
+// input instead of zero-initialized registers, which lets the register
+// allocator keep every accumulator in place across the k-loop.
+__device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_first(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
 struct BRegs {
   u32x2 c[NS];
 };
@@ -103,25 +120,26 @@ struct TileCtx {
 };
 
 template <bool kGateUp, int MSUB>
-__device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* A0, uint16_t* A1,
-                                          uint16_t* A2, uint16_t* A3, uint16_t* Ssh, uint16_t* Bsh) {
+__device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* __restrict__ A0,
+                                          uint16_t* __restrict__ A1, uint16_t* __restrict__ A2,
+                                          uint16_t* __restrict__ Ssh, uint16_t* __restrict__ Bsh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const bool ping = wave < NWAVES / 2;  // MFMA-first half of the waves
   const int Kd = g.Kdim;
   const int gpr = Kd / 64;  // quant groups per weight row
   constexpr int AROWS = MSUB * 16;
-  constexpr int ADMA = (AROWS + 63) / 64;  // 1-KB LDS-DMA writes per wave per stage
+  constexpr int ROWS_PER_DMA = 8 * NWAVES;                         // one 1-KB write per wave covers 8 rows
+  constexpr int ADMA = (AROWS + ROWS_PER_DMA - 1) / ROWS_PER_DMA;  // LDS-DMA writes per wave per stage
 
   // Activation staging by direct-to-LDS loads: per stage, DMA i of wave w
-  // fills tile rows 8w + 64i .. +7 (1 KB, 16 B per lane).  Lane l lands at
-  // row 8w + 64i + l/8, physical chunk l%8, so it fetches the logical chunk
+  // fills tile rows 32i + 8w .. +7 (1 KB, 16 B per lane).  Lane l lands at
+  // row 32i + 8w + l/8, physical chunk l%8, so it fetches the logical chunk
   // that the swizzle maps there.  Rows past the group read zeros (the DMAs
-  // past the live subtiles stay inside the 256-row slot and are never read).
+  // past the live subtiles stay inside the slot and are never read).
   uint32_t adoff[ADMA];
 #pragma unroll
   for (int i = 0; i < ADMA; ++i) {
-    const int r = 8 * wave + 64 * i + (lane >> 3);
+    const int r = ROWS_PER_DMA * i + 8 * wave + (lane >> 3);
     const int c = swz(r, lane & 7);  // swz is an involution
     adoff[i] = kOob;
     if (r < t.nrows) {
@@ -133,20 +151,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     }
   }
 
-  f32x4 acc[MSUB][NS];
-#pragma unroll
-  for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-    for (int j = 0; j < NS; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  BRegs bq[4];
-  bf16x8 bf[2][NS][2];
+  f32x4 acc[MSUB][NS];  // first written by the k-step-0 MFMAs of stage 0
+  BRegs bq[3];          // codes of three consecutive stages
+  bf16x8 bf[NS][2];     // dequantized B fragments of the current stage
 
   auto dma_a = [&](uint16_t* slot, int kt) {
 #pragma unroll
     for (int i = 0; i < ADMA; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(t.a_rs, (__attribute__((address_space(3))) void*)(slot + (8 * wave + 64 * i) * BK),
-                                                 16, adoff[i], kt * BK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          t.a_rs, (__attribute__((address_space(3))) void*)(slot + (ROWS_PER_DMA * i + 8 * wave) * BK), 16, adoff[i],
+          kt * BK * 2, 0, 0);
   };
   // Wait until this wave's DMA writes into `slot` have landed: a dummy LDS
   // read of the slot makes the compiler insert the matching vmcnt wait.
@@ -159,14 +173,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     for (int j = 0; j < NS; ++j)
       q.c[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.c_rs, t.c_off[j], kt * 32, 0));
   };
-  // scale and bias of stage kt's quant group, from the tile's LDS tables
-  auto dequant = [&](const BRegs& q, bf16x8 (&dst)[NS][2], int kt) {
+  // Dequantize stage kt's codes into bf, with each subtile's scale and bias
+  // from the tile's LDS tables.
+  auto dequant = [&](const BRegs& q, int kt) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int idx = t.sb_row[j] * gpr + kt;
-      const float s = bf16_bits_to_f32(Ssh[idx]), b = bf16_bits_to_f32(Bsh[idx]);
-      dst[j][0] = dequant8(q.c[j][0], s, b);
-      dst[j][1] = dequant8(q.c[j][1], s, b);
+      const float sv = bf16_bits_to_f32(Ssh[idx]), bv = bf16_bits_to_f32(Bsh[idx]);
+      bf[j][0] = dequant8(q.c[j][0], sv, bv);
+      bf[j][1] = dequant8(q.c[j][1], sv, bv);
     }
   };
   // The tile's scales and biases for the whole reduction: one or two
@@ -195,16 +210,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     const int r = m * 16 + ln;
     return *reinterpret_cast<const bf16x8*>(&Ab[r * BK + swz(r, 2 * lg + st) * 8]);
   };
-  auto mfmas = [&](const bf16x8 (&bcur)[NS][2], const uint16_t* Ab) {
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      const bf16x8 a0 = a_frag(Ab, m, 0), a1 = a_frag(Ab, m, 1);
-#pragma unroll
-      for (int j = 0; j < NS; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bcur[j][0], acc[m][j], 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < NS; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bcur[j][1], acc[m][j], 0, 0, 0);
-    }
-  };
 
   // Every wave issues the same, unconditional sequence of loads (stage
   // indices clamped at the end, rows past the group reading zeros), so the
@@ -217,58 +222,83 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   load_b(bq[0], 0);
   dma_a(A1, min(1, last));
   load_b(bq[1], min(1, last));
-  dma_a(A2, min(2, last));
   load_b(bq[2], min(2, last));
-  load_b(bq[3], min(3, last));
   wait_slot(Ssh);
   wait_slot(Bsh);
   wait_slot(A0);
   __builtin_amdgcn_s_barrier();
-  dequant(bq[0], bf[0], 0);
+  dequant(bq[0], 0);
 
-  // Stage kt (ring slot kt%4): MFMAs on the slot with the B fragments
-  // dequantized during the previous stage, and the dequant of stage kt+1
-  // (order set by the ping/pong half); then DMA stage kt+3 into the slot read
-  // one stage ago, load the codes of stage kt+4 into the register set just
-  // consumed, wait for this wave's DMA of stage kt+1 (issued two stages ago)
-  // and meet at the barrier (a plain s_barrier: a fenced one would drain
-  // every outstanding load).
-  auto stage = [&](int kt, bf16x8 (&bcur)[NS][2], bf16x8 (&bnext)[NS][2], BRegs& qnext, BRegs& qfree,
-                   const uint16_t* Ab, uint16_t* Anext, uint16_t* Afree) {
-    const bool more = kt + 1 < nk;
-    if (ping) {
-      mfmas(bcur, Ab);
-      if (more) dequant(qnext, bnext, kt + 1);
-    } else {
-      if (more) dequant(qnext, bnext, kt + 1);
-      mfmas(bcur, Ab);
+  // Stage kt (ring slot kt%3, codes bq[kt%3]):
+  //  - DMA stage kt+2 into the slot read in stage kt-1 (free since the last
+  //    barrier) and load the codes of stage kt+3 into bq[kt%3] (dequantized
+  //    at the end of stage kt-1);
+  //  - per 16-row subtile m, one scheduling region with the LDS reads of
+  //    subtile m+1's A fragments and subtile m's 8 MFMAs;
+  //  - dequantize stage kt+1's codes into bf in place (the MFMAs have read
+  //    their operands), wait for this wave's DMA of stage kt+1 and meet at
+  //    the barrier (a plain s_barrier: a fenced one would drain every
+  //    outstanding load).
+  auto stage = [&](auto first, int kt, BRegs& qown, const BRegs& qnext, const uint16_t* Ab,
+                   uint16_t* Anext, uint16_t* Afree) {
+    dma_a(Afree, min(kt + 2, last));
+    load_b(qown, min(kt + 3, last));
+    bf16x8 af[2][2];
+    af[0][0] = a_frag(Ab, 0, 0);
+    af[0][1] = a_frag(Ab, 0, 1);
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+      if (m + 1 < MSUB) {
+        af[(m + 1) & 1][0] = a_frag(Ab, m + 1, 0);
+        af[(m + 1) & 1][1] = a_frag(Ab, m + 1, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if constexpr (decltype(first)::value) mfma_first(acc[m][j], af[m & 1][0], bf[j][0]);
+        else mfma_acc(acc[m][j], af[m & 1][0], bf[j][0]);
+      }
+#pragma unroll
+      for (int j = 0; j < NS; ++j) mfma_acc(acc[m][j], af[m & 1][1], bf[j][1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    dma_a(Afree, min(kt + 3, last));
-    load_b(qfree, min(kt + 4, last));
+    // the last stage dequantizes its own codes again (clamped), unused
+    dequant(qnext, min(kt + 1, last));
     wait_slot(Anext);
     __builtin_amdgcn_s_barrier();
   };
+  const std::integral_constant<bool, true> kFirst;
+  const std::integral_constant<bool, false> kNext;
 
-  for (int kt = 0; kt < nk; kt += 4) {
-    stage(kt, bf[0], bf[1], bq[1], bq[0], A0, A1, A3);
-    if (kt + 1 < nk) stage(kt + 1, bf[1], bf[0], bq[2], bq[1], A1, A2, A0);
-    if (kt + 2 < nk) stage(kt + 2, bf[0], bf[1], bq[3], bq[2], A2, A3, A1);
-    if (kt + 3 < nk) stage(kt + 3, bf[1], bf[0], bq[0], bq[3], A3, A0, A2);
+  // Stage 0 starts the accumulators; then three stages per iteration with no
+  // conditions inside, so the wait counts at the loop head are exact; the
+  // last (nk - 1) % 3 stages follow the loop.
+  stage(kFirst, 0, bq[0], bq[1], A0, A1, A2);
+  int kt = 1;
+  for (; kt + 3 <= nk; kt += 3) {
+    stage(kNext, kt, bq[1], bq[2], A1, A2, A0);
+    stage(kNext, kt + 1, bq[2], bq[0], A2, A0, A1);
+    stage(kNext, kt + 2, bq[0], bq[1], A0, A1, A2);
   }
+  if (kt < nk) stage(kNext, kt, bq[1], bq[2], A1, A2, A0);
+  if (kt + 1 < nk) stage(kNext, kt + 1, bq[2], bq[0], A2, A0, A1);
 
   // ---- epilogue: MFMA 16x16 output layout, lane holds rows 4*lg+i, column ln
   if (kGateUp) {
+    // subtiles 0,1: gate columns; 2,3: the matching up columns
     uint16_t* h = reinterpret_cast<uint16_t*>(g.c);
-    if (t.jval[0]) {
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
+    for (int j = 0; j < NS / 2; ++j) {
+      if (t.jval[j]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m * 16 + 4 * lg + i;
-          if (r < t.nrows) {
-            const float gv = acc[m][0][i], uv = acc[m][1][i];
-            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-            h[(size_t)(t.row0 + r) * g.I + t.ocol[0]] = f32_to_bf16_bits(gv * sig * uv);
+        for (int m = 0; m < MSUB; ++m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + 4 * lg + i;
+            if (r < t.nrows) {
+              const float gv = acc[m][j][i], uv = acc[m][j + NS / 2][i];
+              const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+              h[(size_t)(t.row0 + r) * g.I + t.ocol[j]] = f32_to_bf16_bits(gv * sig * uv);
+            }
           }
         }
       }
@@ -291,13 +321,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
 }
 
 template <bool kGateUp>
-__global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
-  // activation ring: four stages of [256 rows][64] bf16 (separate objects so
+__global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
+  // activation ring: three stages of [128 rows][64] bf16 (separate objects so
   // the compiler tracks the direct-to-LDS loads of each slot on its own)
   __shared__ __attribute__((aligned(16))) uint16_t A0[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t A1[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t A2[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t A3[BM * BK];
   // the tile's scales and biases: [256 weight rows][<= 32 groups] bf16 each
   __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kMaxGroups];
   __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kMaxGroups];
@@ -346,17 +375,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
   // This lane's weight rows (one per 16-column subtile).  Subtiles past the
   // matrix edge read row 0 and are never stored.
   if (kGateUp) {
-    // subtile 0: gate rows hc..hc+15; subtile 1: the matching up rows I + hc..
-    const int hc = nb * (BN / 2) + wave * 16;
-    const bool v = hc < g.I;
-    t.jval[0] = t.jval[1] = v;
-    t.ocol[0] = t.ocol[1] = hc + ln;
-    const uint32_t rg = v ? hc + ln : 0, ru = v ? g.I + hc + ln : 0;
-    t.c_off[0] = rg * cpr + 8u * lg;
-    t.c_off[1] = ru * cpr + 8u * lg;
-    // scale/bias tables: rows 0..127 = gate rows nb*128.., 128..255 = up rows
-    t.sb_row[0] = wave * 16 + ln;
-    t.sb_row[1] = BN / 2 + wave * 16 + ln;
+    // subtiles 0,1: gate rows hc..hc+31; subtiles 2,3: the matching up rows
+    // I + hc..  (hc = this wave's first gate row)
+    const int hc = nb * (BN / 2) + wave * (WN / 2);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int jj = j % (NS / 2);
+      const int row = hc + 16 * jj;
+      const bool v = row < g.I;
+      t.jval[j] = v;
+      t.ocol[j] = row + ln;
+      const uint32_t r = v ? (j < NS / 2 ? 0 : g.I) + row + ln : 0;
+      t.c_off[j] = r * cpr + 8u * lg;
+      // scale/bias tables: rows 0..127 = gate rows nb*128.., 128..255 = up rows
+      t.sb_row[j] = (j < NS / 2 ? 0 : BN / 2) + wave * (WN / 2) + 16 * jj + ln;
+    }
     t.sb_half = (BN / 2) * gpr * 2 / 16;
     t.sb_src[0] = (uint32_t)(nb * (BN / 2)) * gpr * 2u;
     t.sb_src[1] = (uint32_t)(g.I + nb * (BN / 2)) * gpr * 2u;
@@ -378,22 +411,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4_kernel(GemmArgs g) {
 
   const int msub = (t.nrows + 15) >> 4;
   switch (msub) {
-    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
-    default: tile_body<kGateUp, 16>(g, t, A0, A1, A2, A3, Ssh, Bsh); break;
+    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    default: tile_body<kGateUp, 8>(g, t, A0, A1, A2, Ssh, Bsh); break;
   }
 }
 
