@@ -163,10 +163,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
           kt * BK * 2, 0, 0);
   };
   // Wait until this wave's DMA writes into `slot` have landed: a dummy LDS
-  // read of the slot makes the compiler insert the matching vmcnt wait.
+  // read inside every region the wave's DMAs wrote makes the compiler insert
+  // the vmcnt wait for the last of them (it tracks direct-to-LDS loads per
+  // address range, so one read would only wait for the DMA that covers it).
   auto wait_slot = [&](const uint16_t* slot) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + 8 * wave * BK + 2 * lane);
-    asm volatile("" ::"v"(v));
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (ROWS_PER_DMA * i + 8 * wave) * BK + 2 * lane);
+      asm volatile("" ::"v"(v));
+    }
   };
   auto load_b = [&](BRegs& q, int kt) {
 #pragma unroll
@@ -223,10 +228,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   dma_a(A1, min(1, last));
   load_b(bq[1], min(1, last));
   load_b(bq[2], min(2, last));
-  wait_slot(Ssh);
-  wait_slot(Bsh);
-  wait_slot(A0);
-  __builtin_amdgcn_s_barrier();
+  __syncthreads();  // every wave's DMAs of the tables and of stage 0 landed
   dequant(bq[0], 0);
 
   // Stage kt (ring slot kt%3, codes bq[kt%3]):

@@ -6,6 +6,8 @@
 // "GPU 상주와 메모리 절감").
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moeq4 {
@@ -58,23 +60,202 @@ __global__ __launch_bounds__(64) void route_wnorm_kernel(const uint16_t* __restr
 namespace {
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset that reads as zero
 __device__ __forceinline__ rsrc_t rsrc_of(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
-constexpr int kWChunk = 64;  // hidden columns of the router weight staged per LDS chunk
-// 16-byte chunk swizzle of a 128-byte LDS row (rows are experts)
-__device__ __forceinline__ int wswz(int row, int c) { return c ^ (row & 7); }
+// 16-byte-chunk swizzle of a 128-byte LDS row (conflict-free MFMA fragment
+// reads for 16 consecutive rows); an involution.
+__device__ __forceinline__ int rswz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
+constexpr int kLgTok = 64;   // tokens per approximate-logits workgroup
+constexpr int kLgK = 64;     // hidden columns per stage
+constexpr int kXfPad = 4;    // fp32 padding per staged token row (bank spread)
 }  // namespace
 
-__global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a, int32_t* __restrict__ hist,
-                                                         const float* __restrict__ wn) {
+// ---------------------------------------------------------------------------
+// Approximate router logits a[t,e] = sum_h x[t,h] w[e,h] (+ bias) on bf16 MFMA
+// with fp32 accumulation, plus the token row norms ||x_t||.
+//
+// One workgroup: 64 tokens x all (<= 256) experts; wave w owns experts
+// 64w..64w+63 for all 64 tokens (a 64x64 register tile per wave, so every
+// fragment read from LDS feeds four MFMAs).  Token and router rows stream
+// through a 3-slot LDS ring of 64-column stages filled by direct-to-LDS
+// loads two stages ahead.  Every MFMA adds a 32-product step to its fp32
+// accumulator, the structure the selection kernel's error bound assumes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, float* __restrict__ alog,
+                                                           float* __restrict__ xnorm) {
+  __shared__ __attribute__((aligned(16))) uint16_t ring[3 * (kLgTok + MOE_MAX_EXPERTS) * kLgK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int t0 = blockIdx.x * kLgTok;
+  const int T = a.T, H = a.H, E = a.E;
+  const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
+  const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
+  constexpr int kSlot = (kLgTok + MOE_MAX_EXPERTS) * kLgK;  // x rows then router rows
+  uint16_t* __restrict__ S0 = ring;
+  uint16_t* __restrict__ S1 = ring + kSlot;
+  uint16_t* __restrict__ S2 = ring + 2 * kSlot;
+
+  // DMA plan per stage: wave w fills x rows 16w + 8i + lane/8 (i < 2) and
+  // router rows 64w + 8i + lane/8 (i < 8); lane l writes 16 B at physical
+  // chunk l%8 of its row, fetching the logical chunk the swizzle maps there.
+  uint32_t xoff[2], woff[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    xoff[i] = t0 + r < T ? ((uint32_t)(t0 + r) * H + 8u * rswz(r, lane & 7)) * 2u : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 64 * wave + 8 * i + (lane >> 3);
+    woff[i] = r < E ? ((uint32_t)r * H + 8u * rswz(r, lane & 7)) * 2u : kOob;
+  }
+  auto dma = [&](uint16_t* slot, int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_rs, (__attribute__((address_space(3))) void*)(slot + (16 * wave + 8 * i) * kLgK), 16, xoff[i],
+          kt * kLgK * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rs, (__attribute__((address_space(3))) void*)(slot + (kLgTok + 64 * wave + 8 * i) * kLgK), 16, woff[i],
+          kt * kLgK * 2, 0, 0);
+  };
+  // Wait for this wave's DMAs into `slot`: a dummy LDS read inside every
+  // region they wrote makes the compiler wait for the last of them (it
+  // tracks direct-to-LDS loads per address range).
+  auto wait_slot = [&](const uint16_t* slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (16 * wave + 8 * i) * kLgK + 2 * lane);
+      asm volatile("" ::"v"(v));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (kLgTok + 64 * wave + 8 * i) * kLgK + 2 * lane);
+      asm volatile("" ::"v"(v));
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float s2 = 0.0f;  // partial sum of squares of token row tid/4, columns 16*(tid%4).. of each stage
+
+  auto stage = [&](int kt, const uint16_t* Sb) {
+    // x row norms from the staged bf16 row segment
+    {
+      const int r = tid >> 2, q = tid & 3;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&Sb[r * kLgK + rswz(r, 2 * q + c) * 8]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = bf16_bits_to_f32(v[i] & 0xFFFFu), hi = bf16_bits_to_f32(v[i] >> 16);
+          s2 = __builtin_fmaf(lo, lo, s2);
+          s2 = __builtin_fmaf(hi, hi, s2);
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8 av[4], bv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * m + ln;
+        av[m] = *reinterpret_cast<const bf16x8*>(&Sb[r * kLgK + rswz(r, 2 * lg + st) * 8]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 64 * wave + 16 * j + ln;
+        bv[j] = *reinterpret_cast<const bf16x8*>(&Sb[(kLgTok + r) * kLgK + rswz(r, 2 * lg + st) * 8]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv[j], acc[m][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = H / kLgK;
+  const int last = nk - 1;
+  dma(S0, 0);
+  dma(S1, min(1, last));
+  wait_slot(S0);
+  __syncthreads();
+  // stage kt first DMAs stage kt+2 into the slot read in stage kt-1 (free
+  // since the last barrier), then computes on slot kt%3 and waits for its
+  // own DMA of stage kt+1 before the barrier
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    dma(S2, min(kt + 2, last));
+    stage(kt, S0);
+    wait_slot(S1);
+    __builtin_amdgcn_s_barrier();
+    dma(S0, min(kt + 3, last));
+    stage(kt + 1, S1);
+    wait_slot(S2);
+    __builtin_amdgcn_s_barrier();
+    dma(S1, min(kt + 4, last));
+    stage(kt + 2, S2);
+    wait_slot(S0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (kt < nk) {
+    dma(S2, min(kt + 2, last));
+    stage(kt, S0);
+    wait_slot(S1);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (kt + 1 < nk) {
+    dma(S0, min(kt + 3, last));
+    stage(kt + 1, S1);
+    wait_slot(S2);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // norms: the 4 threads of a token row are adjacent lanes
+  s2 += __shfl_xor(s2, 1);
+  s2 += __shfl_xor(s2, 2);
+  if ((tid & 3) == 0 && t0 + (tid >> 2) < T) xnorm[t0 + (tid >> 2)] = sqrtf(s2);
+  // approximate logits (+ bias); MFMA layout: lane holds rows 4*lg+i, column ln
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * wave + 16 * j + ln;
+    if (e < E) {
+      const float rb = a.router_bias ? a.router_bias[e] : 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * m + 4 * lg + i;
+          if (t < T) alog[(size_t)t * E + e] = acc[m][j][i] + rb;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection: candidates from the approximate logits, canonical fp32 chains
+// for the candidates only, exact top-k and combine weights, and this block's
+// expert histogram.  One workgroup = 16 tokens, 16 lanes per token for the
+// per-token steps; the chains of all 16 tokens are packed one per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
+                                                           const float* __restrict__ xnorm,
+                                                           const float* __restrict__ wn,
+                                                           int32_t* __restrict__ hist) {
   constexpr int TB = kRouteTokens;  // 16 tokens
-  __shared__ __attribute__((aligned(16))) uint16_t xs[TB * MOE_MAX_REDUCTION];          // token rows, bf16
-  __shared__ __attribute__((aligned(16))) uint16_t wsm[2][MOE_MAX_EXPERTS * kWChunk];   // router chunk ring
-  __shared__ __attribute__((aligned(16))) float lv[TB][MOE_MAX_EXPERTS];  // approx logits, then exact values
+  // token rows in fp32 (padded rows spread the chains' reads over the banks)
+  __shared__ __attribute__((aligned(16))) float xf[TB * (MOE_MAX_REDUCTION + kXfPad)];
+  __shared__ float lv[TB][MOE_MAX_EXPERTS];  // canonical values of the candidates
   __shared__ short cand[TB][MOE_MAX_EXPERTS];
-  __shared__ int ccount[TB];
-  __shared__ float xnorm[TB];
+  __shared__ int ccount[TB], cstart[TB + 1];
   __shared__ float wmax_s;
   __shared__ int bhist[MOE_MAX_EXPERTS];
 
@@ -82,28 +263,23 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a, int32_t* _
   const int ln = lane & 15, lg = lane >> 4;
   const int t0 = blockIdx.x * TB;
   const int T = a.T, H = a.H, E = a.E, K = a.K;
+  const int xstride = H + kXfPad;
   const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
   const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
 
   bhist[tid] = 0;
-  // ---- phase 0: stage the 16 token rows (bf16) and their 2-norms ----------
+  // ---- token rows to fp32 in LDS; largest router-row norm -----------------
   {
     const int tt = tid >> 4, seg = tid & 15;
-    float s2 = 0.0f;
     for (int h = 8 * seg; h < H; h += 128) {
-      const u32x4 v = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, (uint32_t)((t0 + tt) * H + h) * 2u, 0, 0));
-      *reinterpret_cast<u32x4*>(&xs[tt * H + h]) = v;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_bits_to_f32(v[q] & 0xFFFFu), hi = bf16_bits_to_f32(v[q] >> 16);
-        s2 = __builtin_fmaf(lo, lo, s2);
-        s2 = __builtin_fmaf(hi, hi, s2);
-      }
+      const uint32_t off = t0 + tt < T ? (uint32_t)((t0 + tt) * H + h) * 2u : kOob;
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+      float4* dst = reinterpret_cast<float4*>(&xf[tt * xstride + h]);
+      dst[0] = float4{bf16_bits_to_f32(v[0] & 0xFFFFu), bf16_bits_to_f32(v[0] >> 16), bf16_bits_to_f32(v[1] & 0xFFFFu),
+                      bf16_bits_to_f32(v[1] >> 16)};
+      dst[1] = float4{bf16_bits_to_f32(v[2] & 0xFFFFu), bf16_bits_to_f32(v[2] >> 16), bf16_bits_to_f32(v[3] & 0xFFFFu),
+                      bf16_bits_to_f32(v[3] >> 16)};
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, 16);
-    if (seg == 0) xnorm[tt] = sqrtf(s2);
     if (wave == 0) {
       float m = 0.0f;
       for (int e = lane; e < E; e += 64) m = fmaxf(m, wn[e]);
@@ -112,43 +288,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a, int32_t* _
       if (lane == 0) wmax_s = m;
     }
   }
-
-  // ---- phase 1: approximate logits on the matrix cores ---------------------
-  // rows = the 16 tokens, columns = experts 64*wave + 16j + ln (j = 0..3)
-  {
-    f32x4 acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t xo = (uint32_t)((t0 + ln) * H + 8 * lg) * 2u;
-    uint32_t wo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wo[j] = (uint32_t)((64 * wave + 16 * j + ln) * H + 8 * lg) * 2u;
-#pragma unroll 8
-    for (int k0 = 0; k0 < H; k0 += 32) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(x_rs, xo, k0 * 2, 0));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wo[j], k0 * 2, 0));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 64 * wave + 16 * j + ln;
-      const float rb = (a.router_bias && e < E) ? a.router_bias[e] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lv[4 * lg + i][e] = e < E ? acc[j][i] + rb : -INFINITY;
-    }
-  }
   __syncthreads();
 
-  // ---- phase 2: candidates per token (16 lanes per token) ------------------
+  // ---- candidates per token (16 lanes per token) ------------------------
   const int tok = 4 * wave + lg;  // this 16-lane group's token
   const bool tvalid = t0 + tok < T;
   {
     float v[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = lv[tok][16 * ln + q];
+    for (int q = 0; q < 16; ++q) {
+      const int e = 16 * ln + q;
+      v[q] = (tvalid && e < E) ? alog[(size_t)(t0 + tok) * E + e] : -INFINITY;
+    }
     uint32_t taken = 0;
     float tau = -INFINITY;
     for (int k = 0; k < K; ++k) {
@@ -178,7 +329,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a, int32_t* _
     if (!a.norm_topk) {
       win = INFINITY;
     } else {
-      const float S = xnorm[tok] * wmax_s * 1.001f;
+      const float S = (tvalid ? xnorm[t0 + tok] : 0.0f) * wmax_s * 1.001f;
       const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
       const float dc = (float)(H + 2) * 0x1p-24f * S;
       win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
@@ -201,66 +352,70 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a, int32_t* _
     if (ln == 15) ccount[tok] = tvalid ? incl : 0;
   }
   __syncthreads();
-
-  // ---- phase 3: canonical chains for the candidates -------------------------
-  // Router rows are streamed in 64-column chunks through an LDS ring (one
-  // full cache line per row and chunk); every 16-lane group runs the chains
-  // of its token's candidates, 16 at a time.
-  int maxc = 0;
-#pragma unroll
-  for (int t = 0; t < TB; ++t) maxc = max(maxc, ccount[t]);
-  const int C = ccount[tok];
-  for (int base = 0; base < maxc; base += 16) {
-    const int c = base + ln;
-    const bool live = c < C;
-    const int e = live ? cand[tok][c] : 0;
-    float acc = 0.0f;
-    // 256 rows x 128 B per chunk: lane -> row tid/8 + 32*i, 16-byte chunk tid%8.
-    // The next chunk's loads go out before this chunk's chains and land in
-    // LDS after them, so their latency hides under the arithmetic.
-    u32x4 wreg[8];
-    auto load_w = [&](int h0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 3) + 32 * i, ch = tid & 7;
-        wreg[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, (uint32_t)(r * H + h0 + 8 * ch) * 2u, 0, 0));
-      }
-    };
-    auto store_w = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 3) + 32 * i, ch = tid & 7;
-        *reinterpret_cast<u32x4*>(&wsm[buf][r * kWChunk + wswz(r, ch) * 8]) = wreg[i];
-      }
-    };
-    load_w(0);
-    store_w(0);
-    __syncthreads();
-    for (int h0 = 0; h0 < H; h0 += kWChunk) {
-      const int buf = (h0 / kWChunk) & 1;
-      const bool more = h0 + kWChunk < H;
-      if (more) load_w(h0 + kWChunk);
-      if (live) {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(&xs[tok * H + h0 + 8 * ch]);
-          const u32x4 wv = *reinterpret_cast<const u32x4*>(&wsm[buf][e * kWChunk + wswz(e, ch) * 8]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc = __builtin_fmaf(bf16_bits_to_f32(xv[q] & 0xFFFFu), bf16_bits_to_f32(wv[q] & 0xFFFFu), acc);
-            acc = __builtin_fmaf(bf16_bits_to_f32(xv[q] >> 16), bf16_bits_to_f32(wv[q] >> 16), acc);
-          }
-        }
-      }
-      if (more) store_w(buf ^ 1);
-      __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < TB; ++t) {
+      cstart[t] = run;
+      run += ccount[t];
     }
-    if (live) lv[tok][c] = (a.router_bias ? acc + a.router_bias[e] : acc);
+    cstart[TB] = run;
   }
   __syncthreads();
 
-  // ---- phase 4: exact top-k among the candidates ----------------------------
+  // ---- canonical chains: l = sum_h x[t,h] w[e,h] in fp32, h ascending ------
+  // Chain c of the block's list runs on thread c % 256 (batch c / 256); the
+  // router row streams from L2 in 16-byte pieces P pieces ahead (32 covers
+  // the L2 latency; 8 where H is not a multiple of 256, since the unrolled
+  // body walks whole groups of P pieces), the token row comes from LDS.
+  // bf16 x bf16 products are exact in fp32, so each fma rounds exactly like
+  // "acc = acc + x*w".
+  const int npc = H / 8;
+  auto chains = [&](auto depth) {
+    constexpr int P = decltype(depth)::value;
+    const int total = cstart[TB];
+    for (int c = tid; c < ((total + 255) / 256) * 256; c += 256) {
+      const bool live = c < total;
+      int tk = 0;
+#pragma unroll
+      for (int t = 1; t < TB; ++t) tk += (live && c >= cstart[t]) ? 1 : 0;
+      const int slot = c - cstart[tk];
+      const int e = live ? cand[tk][slot] : 0;
+      const uint32_t wrow = live ? (uint32_t)e * H * 2u : kOob;
+      const float* xr = &xf[tk * xstride];
+      u32x4 wb[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * min(i, npc - 1), 0));
+      float acc = 0.0f;
+      for (int p0 = 0; p0 < npc; p0 += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const u32x4 w = wb[i];
+          wb[i] = __builtin_bit_cast(u32x4,
+                                     __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * min(p0 + i + P, npc - 1), 0));
+          const float4 x0 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i)]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i) + 4]);
+          acc = __builtin_fmaf(x0.x, bf16_bits_to_f32(w[0] & 0xFFFFu), acc);
+          acc = __builtin_fmaf(x0.y, bf16_bits_to_f32(w[0] >> 16), acc);
+          acc = __builtin_fmaf(x0.z, bf16_bits_to_f32(w[1] & 0xFFFFu), acc);
+          acc = __builtin_fmaf(x0.w, bf16_bits_to_f32(w[1] >> 16), acc);
+          acc = __builtin_fmaf(x1.x, bf16_bits_to_f32(w[2] & 0xFFFFu), acc);
+          acc = __builtin_fmaf(x1.y, bf16_bits_to_f32(w[2] >> 16), acc);
+          acc = __builtin_fmaf(x1.z, bf16_bits_to_f32(w[3] & 0xFFFFu), acc);
+          acc = __builtin_fmaf(x1.w, bf16_bits_to_f32(w[3] >> 16), acc);
+        }
+      }
+      if (live) lv[tk][slot] = a.router_bias ? acc + a.router_bias[e] : acc;
+    }
+  };
+  if (npc % 32 == 0)
+    chains(std::integral_constant<int, 32>{});
+  else
+    chains(std::integral_constant<int, 8>{});
+  __syncthreads();
+  const int C = ccount[tok];
+
+  // ---- exact top-k among the candidates ----------------------------------
   if (tvalid) {
     const int t = t0 + tok;
     uint32_t taken = 0;  // bit r: candidate ln + 16 r taken
@@ -453,19 +608,39 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
   }
 }
 
-size_t route_workspace_bytes(int T, int E) {
+namespace {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+struct RouteWs {
+  size_t hist, wn, alog, xnorm, total;
+};
+RouteWs route_ws_layout(int T, int E) {
   const size_t nb = (size_t)(T + kRouteTokens - 1) / kRouteTokens;
-  return nb * (size_t)E * sizeof(int32_t) + 256 * sizeof(float);  // block histograms + router row norms
+  RouteWs L;
+  L.hist = 0;                                                     // per-block expert histograms
+  L.wn = align256(nb * (size_t)E * sizeof(int32_t));             // router row norms
+  L.alog = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));      // approximate logits [T][E]
+  L.xnorm = L.alog + align256((size_t)T * E * sizeof(float));     // token row norms
+  L.total = L.xnorm + align256((size_t)T * sizeof(float));
+  return L;
 }
+}  // namespace
+
+size_t route_workspace_bytes(int T, int E) { return route_ws_layout(T, E).total; }
 
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
-  int32_t* hist = reinterpret_cast<int32_t*>(ws);
-  float* wn = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (size_t)nb * a.E * sizeof(int32_t));
+  const RouteWs L = route_ws_layout(a.T, a.E);
+  char* base = reinterpret_cast<char*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
+  float* wn = reinterpret_cast<float*>(base + L.wn);
+  float* alog = reinterpret_cast<float*>(base + L.alog);
+  float* xnorm = reinterpret_cast<float*>(base + L.xnorm);
   hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(nb), dim3(256), 0, stream, a, hist, wn);
+  hipLaunchKernelGGL(route_logits_kernel, dim3((a.T + kLgTok - 1) / kLgTok), dim3(256), 0, stream, a, alog, xnorm);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(route_select_kernel, dim3(nb), dim3(256), 0, stream, a, alog, xnorm, wn, hist);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, nb, a.T, a.K, a.E,
                      a.has_shared, a.out);
