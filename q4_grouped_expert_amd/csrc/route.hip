@@ -67,178 +67,180 @@ __device__ __forceinline__ rsrc_t rsrc_of(const void* p, uint32_t bytes) {
 // 16-byte-chunk swizzle of a 128-byte LDS row (conflict-free MFMA fragment
 // reads for 16 consecutive rows); an involution.
 __device__ __forceinline__ int rswz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
-constexpr int kLgTok = 64;   // tokens per approximate-logits workgroup
+constexpr int kLgTile = 64;  // tokens and experts per approximate-logits workgroup
 constexpr int kLgK = 64;     // hidden columns per stage
+// s_waitcnt that bounds only the vector-memory counter (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 constexpr int kXfPad = 4;    // fp32 padding per staged token row (bank spread)
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Approximate router logits a[t,e] = sum_h x[t,h] w[e,h] (+ bias) on bf16 MFMA
-// with fp32 accumulation, plus the token row norms ||x_t||.
+// with fp32 accumulation.
 //
-// One workgroup: 64 tokens x all (<= 256) experts; wave w owns experts
-// 64w..64w+63 for all 64 tokens (a 64x64 register tile per wave, so every
-// fragment read from LDS feeds four MFMAs).  Token and router rows stream
-// through a 3-slot LDS ring of 64-column stages filled by direct-to-LDS
-// loads two stages ahead.  Every MFMA adds a 32-product step to its fp32
-// accumulator, the structure the selection kernel's error bound assumes.
+// One workgroup: 64 tokens x 64 experts; wave w owns the 32 x 32 quadrant
+// (tokens 32 (w & 1).., experts 32 (w >> 1)..) as 2 x 2 MFMA tiles.  Token
+// and router rows stream through a 3-slot LDS ring of 64-column stages
+// filled by direct-to-LDS loads two stages ahead.  Every MFMA adds a
+// 32-product step to its fp32 accumulator, the structure the selection
+// kernel's error bound assumes.
+//
+// Block order: consecutive workgroup ids land on consecutive XCDs, so id b
+// takes token tile 8 (b / 8 / neb) + b % 8 and expert tile (b / 8) % neb:
+// the neb workgroups that share a token tile run on one XCD and share its
+// L2.  Ids past the last token tile exit at once.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, float* __restrict__ alog,
-                                                           float* __restrict__ xnorm) {
-  __shared__ __attribute__((aligned(16))) uint16_t ring[3 * (kLgTok + MOE_MAX_EXPERTS) * kLgK];
+__global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb, int neb, float* __restrict__ alog) {
+  constexpr int kRows = 2 * kLgTile;            // token rows, then router rows
+  constexpr int kSlot = kRows * kLgK;           // bf16 elements per ring slot
+  __shared__ __attribute__((aligned(16))) uint16_t ring[3 * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * kLgTok;
+  const int q = blockIdx.x >> 3;
+  const int tb = (q / neb) * 8 + (blockIdx.x & 7), eb = q % neb;
+  if (tb >= ntb) return;
+  const int t0 = tb * kLgTile, e0 = eb * kLgTile;
   const int T = a.T, H = a.H, E = a.E;
   const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
   const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
-  constexpr int kSlot = (kLgTok + MOE_MAX_EXPERTS) * kLgK;  // x rows then router rows
-  uint16_t* __restrict__ S0 = ring;
-  uint16_t* __restrict__ S1 = ring + kSlot;
-  uint16_t* __restrict__ S2 = ring + 2 * kSlot;
 
-  // DMA plan per stage: wave w fills x rows 16w + 8i + lane/8 (i < 2) and
-  // router rows 64w + 8i + lane/8 (i < 8); lane l writes 16 B at physical
-  // chunk l%8 of its row, fetching the logical chunk the swizzle maps there.
-  uint32_t xoff[2], woff[8];
+  // DMA plan per stage: wave w fills token rows 16w + 8i + lane/8 and router
+  // rows 16w + 8i + lane/8 (i < 2); lane l writes 16 B at physical chunk l%8
+  // of its row, fetching the logical chunk the swizzle maps there.  Rows
+  // past T or E read as zero.
+  uint32_t xoff[2], woff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 16 * wave + 8 * i + (lane >> 3);
     xoff[i] = t0 + r < T ? ((uint32_t)(t0 + r) * H + 8u * rswz(r, lane & 7)) * 2u : kOob;
+    woff[i] = e0 + r < E ? ((uint32_t)(e0 + r) * H + 8u * rswz(r, lane & 7)) * 2u : kOob;
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 64 * wave + 8 * i + (lane >> 3);
-    woff[i] = r < E ? ((uint32_t)r * H + 8u * rswz(r, lane & 7)) * 2u : kOob;
-  }
-  auto dma = [&](uint16_t* slot, int kt) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x_rs, (__attribute__((address_space(3))) void*)(slot + (16 * wave + 8 * i) * kLgK), 16, xoff[i],
-          kt * kLgK * 2, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rs, (__attribute__((address_space(3))) void*)(slot + (kLgTok + 64 * wave + 8 * i) * kLgK), 16, woff[i],
-          kt * kLgK * 2, 0, 0);
-  };
-  // Wait for this wave's DMAs into `slot`: a dummy LDS read inside every
-  // region they wrote makes the compiler wait for the last of them (it
-  // tracks direct-to-LDS loads per address range).
-  auto wait_slot = [&](const uint16_t* slot) {
+  constexpr int kDmaPerStage = 4;  // direct-to-LDS loads per wave per stage
+  auto dma = [&](int slot, int kt) {
+    uint16_t* S = ring + slot * kSlot;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (16 * wave + 8 * i) * kLgK + 2 * lane);
-      asm volatile("" ::"v"(v));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (kLgTok + 64 * wave + 8 * i) * kLgK + 2 * lane);
-      asm volatile("" ::"v"(v));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_rs, (__attribute__((address_space(3))) void*)(S + (16 * wave + 8 * i) * kLgK), 16, xoff[i],
+          kt * kLgK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rs, (__attribute__((address_space(3))) void*)(S + (kLgTile + 16 * wave + 8 * i) * kLgK), 16, woff[i],
+          kt * kLgK * 2, 0, 0);
     }
   };
 
-  f32x4 acc[4][4];
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[2][2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float s2 = 0.0f;  // partial sum of squares of token row tid/4, columns 16*(tid%4).. of each stage
-
-  auto stage = [&](int kt, const uint16_t* Sb) {
-    // x row norms from the staged bf16 row segment
-    {
-      const int r = tid >> 2, q = tid & 3;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&Sb[r * kLgK + rswz(r, 2 * q + c) * 8]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = bf16_bits_to_f32(v[i] & 0xFFFFu), hi = bf16_bits_to_f32(v[i] >> 16);
-          s2 = __builtin_fmaf(lo, lo, s2);
-          s2 = __builtin_fmaf(hi, hi, s2);
-        }
-      }
-    }
+    for (int j = 0; j < 2; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto stage = [&](int slot) {
+    const uint16_t* S = ring + slot * kSlot;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      bf16x8 av[4], bv[4];
+      bf16x8 av[2], bv[2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 16 * m + ln;
-        av[m] = *reinterpret_cast<const bf16x8*>(&Sb[r * kLgK + rswz(r, 2 * lg + st) * 8]);
+      for (int m = 0; m < 2; ++m) {
+        const int r = 32 * wm + 16 * m + ln;
+        av[m] = *reinterpret_cast<const bf16x8*>(&S[r * kLgK + rswz(r, 2 * lg + st) * 8]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 64 * wave + 16 * j + ln;
-        bv[j] = *reinterpret_cast<const bf16x8*>(&Sb[(kLgTok + r) * kLgK + rswz(r, 2 * lg + st) * 8]);
+      for (int j = 0; j < 2; ++j) {
+        const int r = 32 * wn + 16 * j + ln;
+        bv[j] = *reinterpret_cast<const bf16x8*>(&S[(kLgTile + r) * kLgK + rswz(r, 2 * lg + st) * 8]);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv[j], acc[m][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv[j], acc[m][j], 0, 0, 0);
     }
   };
 
+  // Stage kt DMAs stage kt+2 into the slot read in stage kt-1 (free since
+  // the last barrier), computes on slot kt%3, then waits until only its own
+  // DMAs of this stage are in flight (so stage kt+1 has landed) and meets
+  // the other waves at the barrier.  Past the last stage the DMAs repeat
+  // the last one, keeping the count per stage fixed; no other vector-memory
+  // access runs inside the loop, so the count is exact.
   const int nk = H / kLgK;
   const int last = nk - 1;
-  dma(S0, 0);
-  dma(S1, min(1, last));
-  wait_slot(S0);
-  __syncthreads();
-  // stage kt first DMAs stage kt+2 into the slot read in stage kt-1 (free
-  // since the last barrier), then computes on slot kt%3 and waits for its
-  // own DMA of stage kt+1 before the barrier
+  dma(0, 0);
+  dma(1, min(1, last));
+  wait_vmcnt<kDmaPerStage>();
+  __builtin_amdgcn_s_barrier();
   int kt = 0;
   for (; kt + 3 <= nk; kt += 3) {
-    dma(S2, min(kt + 2, last));
-    stage(kt, S0);
-    wait_slot(S1);
-    __builtin_amdgcn_s_barrier();
-    dma(S0, min(kt + 3, last));
-    stage(kt + 1, S1);
-    wait_slot(S2);
-    __builtin_amdgcn_s_barrier();
-    dma(S1, min(kt + 4, last));
-    stage(kt + 2, S2);
-    wait_slot(S0);
-    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      dma((u + 2) % 3, min(kt + u + 2, last));
+      stage(u);
+      wait_vmcnt<kDmaPerStage>();
+      __builtin_amdgcn_s_barrier();
+    }
   }
-  if (kt < nk) {
-    dma(S2, min(kt + 2, last));
-    stage(kt, S0);
-    wait_slot(S1);
-    __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (kt + u < nk) {
+      dma((u + 2) % 3, min(kt + u + 2, last));
+      stage(u);
+      wait_vmcnt<kDmaPerStage>();
+      __builtin_amdgcn_s_barrier();
+    }
   }
-  if (kt + 1 < nk) {
-    dma(S0, min(kt + 3, last));
-    stage(kt + 1, S1);
-    wait_slot(S2);
-    __builtin_amdgcn_s_barrier();
-  }
+  wait_vmcnt<0>();  // no direct-to-LDS write outlives the workgroup
 
-  // norms: the 4 threads of a token row are adjacent lanes
-  s2 += __shfl_xor(s2, 1);
-  s2 += __shfl_xor(s2, 2);
-  if ((tid & 3) == 0 && t0 + (tid >> 2) < T) xnorm[t0 + (tid >> 2)] = sqrtf(s2);
   // approximate logits (+ bias); MFMA layout: lane holds rows 4*lg+i, column ln
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = 64 * wave + 16 * j + ln;
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 32 * wn + 16 * j + ln;
     if (e < E) {
       const float rb = a.router_bias ? a.router_bias[e] : 0.0f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * m + 4 * lg + i;
+          const int t = t0 + 32 * wm + 16 * m + 4 * lg + i;
           if (t < T) alog[(size_t)t * E + e] = acc[m][j][i] + rb;
         }
     }
   }
 }
+
+namespace {
+// acc <- fma(x[q], w[q], acc) for q = 0..7 in order, w eight packed bf16.
+// One asm block, so the compiler cannot unpack a piece of w early (it does
+// so to free registers, and then has to wait for loads still in flight).
+__device__ __forceinline__ float chain8(float acc, float4 x0, float4 x1, u32x4 w) {
+  float t0, t1;
+  asm("v_lshlrev_b32 %[t0], 16, %[w0]\n\t"
+      "v_and_b32 %[t1], 0xffff0000, %[w0]\n\t"
+      "v_fmac_f32 %[acc], %[xa], %[t0]\n\t"
+      "v_fmac_f32 %[acc], %[xb], %[t1]\n\t"
+      "v_lshlrev_b32 %[t0], 16, %[w1]\n\t"
+      "v_and_b32 %[t1], 0xffff0000, %[w1]\n\t"
+      "v_fmac_f32 %[acc], %[xc], %[t0]\n\t"
+      "v_fmac_f32 %[acc], %[xd], %[t1]\n\t"
+      "v_lshlrev_b32 %[t0], 16, %[w2]\n\t"
+      "v_and_b32 %[t1], 0xffff0000, %[w2]\n\t"
+      "v_fmac_f32 %[acc], %[xe], %[t0]\n\t"
+      "v_fmac_f32 %[acc], %[xf], %[t1]\n\t"
+      "v_lshlrev_b32 %[t0], 16, %[w3]\n\t"
+      "v_and_b32 %[t1], 0xffff0000, %[w3]\n\t"
+      "v_fmac_f32 %[acc], %[xg], %[t0]\n\t"
+      "v_fmac_f32 %[acc], %[xh], %[t1]"
+      : [acc] "+v"(acc), [t0] "=&v"(t0), [t1] "=&v"(t1)
+      : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [xa] "v"(x0.x), [xb] "v"(x0.y),
+        [xc] "v"(x0.z), [xd] "v"(x0.w), [xe] "v"(x1.x), [xf] "v"(x1.y), [xg] "v"(x1.z), [xh] "v"(x1.w));
+  return acc;
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // Selection: candidates from the approximate logits, canonical fp32 chains
@@ -247,7 +249,6 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, float* _
 // per-token steps; the chains of all 16 tokens are packed one per lane.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
-                                                           const float* __restrict__ xnorm,
                                                            const float* __restrict__ wn,
                                                            int32_t* __restrict__ hist) {
   constexpr int TB = kRouteTokens;  // 16 tokens
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   __shared__ float lv[TB][MOE_MAX_EXPERTS];  // canonical values of the candidates
   __shared__ short cand[TB][MOE_MAX_EXPERTS];
   __shared__ int ccount[TB], cstart[TB + 1];
-  __shared__ float wmax_s;
+  __shared__ float wmax_s, xn_s[TB];
   __shared__ int bhist[MOE_MAX_EXPERTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -268,18 +269,43 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
 
   bhist[tid] = 0;
-  // ---- token rows to fp32 in LDS; largest router-row norm -----------------
+  // ---- token rows to fp32 in LDS, their norms; largest router-row norm ---
+  // 16 lanes per token, 16-byte pieces 128 columns apart; each lane issues
+  // up to 16 loads before it converts any, so a 2048-column row costs one
+  // memory latency.
   {
     const int tt = tid >> 4, seg = tid & 15;
-    for (int h = 8 * seg; h < H; h += 128) {
-      const uint32_t off = t0 + tt < T ? (uint32_t)((t0 + tt) * H + h) * 2u : kOob;
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
-      float4* dst = reinterpret_cast<float4*>(&xf[tt * xstride + h]);
-      dst[0] = float4{bf16_bits_to_f32(v[0] & 0xFFFFu), bf16_bits_to_f32(v[0] >> 16), bf16_bits_to_f32(v[1] & 0xFFFFu),
-                      bf16_bits_to_f32(v[1] >> 16)};
-      dst[1] = float4{bf16_bits_to_f32(v[2] & 0xFFFFu), bf16_bits_to_f32(v[2] >> 16), bf16_bits_to_f32(v[3] & 0xFFFFu),
-                      bf16_bits_to_f32(v[3] >> 16)};
+    const bool tv = t0 + tt < T;
+    float s2 = 0.0f;
+    for (int hb = 0; hb < H; hb += 2048) {
+      u32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = hb + 128 * i + 8 * seg;
+        const uint32_t off = tv && h < H ? (uint32_t)((t0 + tt) * H + h) * 2u : kOob;
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = hb + 128 * i + 8 * seg;
+        if (h < H) {
+          float f[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f[2 * q] = bf16_bits_to_f32(v[i][q] & 0xFFFFu);
+            f[2 * q + 1] = bf16_bits_to_f32(v[i][q] >> 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) s2 = __builtin_fmaf(f[q], f[q], s2);
+          float4* dst = reinterpret_cast<float4*>(&xf[tt * xstride + h]);
+          dst[0] = float4{f[0], f[1], f[2], f[3]};
+          dst[1] = float4{f[4], f[5], f[6], f[7]};
+        }
+      }
     }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, 16);
+    if (seg == 0) xn_s[tt] = sqrtf(s2);
     if (wave == 0) {
       float m = 0.0f;
       for (int e = lane; e < E; e += 64) m = fmaxf(m, wn[e]);
@@ -329,7 +355,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
     if (!a.norm_topk) {
       win = INFINITY;
     } else {
-      const float S = (tvalid ? xnorm[t0 + tok] : 0.0f) * wmax_s * 1.001f;
+      const float S = xn_s[tok] * wmax_s * 1.001f;
       const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
       const float dc = (float)(H + 2) * 0x1p-24f * S;
       win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
@@ -364,10 +390,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 
   // ---- canonical chains: l = sum_h x[t,h] w[e,h] in fp32, h ascending ------
   // Chain c of the block's list runs on thread c % 256 (batch c / 256); the
-  // router row streams from L2 in 16-byte pieces P pieces ahead (32 covers
-  // the L2 latency; 8 where H is not a multiple of 256, since the unrolled
-  // body walks whole groups of P pieces), the token row comes from LDS.
-  // bf16 x bf16 products are exact in fp32, so each fma rounds exactly like
+  // router row streams from L2 in 16-byte pieces P pieces ahead (P = 16, or
+  // 8 where H is not a multiple of 128, since the unrolled body walks whole
+  // groups of P pieces), the token row comes from LDS.  bf16 x bf16
+  // products are exact in fp32, so each fma rounds exactly like
   // "acc = acc + x*w".
   const int npc = H / 8;
   auto chains = [&](auto depth) {
@@ -380,36 +406,37 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
       for (int t = 1; t < TB; ++t) tk += (live && c >= cstart[t]) ? 1 : 0;
       const int slot = c - cstart[tk];
       const int e = live ? cand[tk][slot] : 0;
-      const uint32_t wrow = live ? (uint32_t)e * H * 2u : kOob;
+      uint32_t wrow = live ? (uint32_t)e * H * 2u : kOob;
       const float* xr = &xf[tk * xstride];
+      // first group in piece order (the loop's waits assume wb[i] was issued
+      // i-th, on entry as on the back edge)
       u32x4 wb[P];
 #pragma unroll
-      for (int i = 0; i < P; ++i)
-        wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * min(i, npc - 1), 0));
+      for (int i = 0; i < P; ++i) {
+        wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * i, 0));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       float acc = 0.0f;
       for (int p0 = 0; p0 < npc; p0 += P) {
+        const int nxt = p0 + P < npc ? p0 + P : p0;  // the last group re-reads itself
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-          const u32x4 w = wb[i];
-          wb[i] = __builtin_bit_cast(u32x4,
-                                     __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * min(p0 + i + P, npc - 1), 0));
           const float4 x0 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i)]);
           const float4 x1 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i) + 4]);
-          acc = __builtin_fmaf(x0.x, bf16_bits_to_f32(w[0] & 0xFFFFu), acc);
-          acc = __builtin_fmaf(x0.y, bf16_bits_to_f32(w[0] >> 16), acc);
-          acc = __builtin_fmaf(x0.z, bf16_bits_to_f32(w[1] & 0xFFFFu), acc);
-          acc = __builtin_fmaf(x0.w, bf16_bits_to_f32(w[1] >> 16), acc);
-          acc = __builtin_fmaf(x1.x, bf16_bits_to_f32(w[2] & 0xFFFFu), acc);
-          acc = __builtin_fmaf(x1.y, bf16_bits_to_f32(w[2] >> 16), acc);
-          acc = __builtin_fmaf(x1.z, bf16_bits_to_f32(w[3] & 0xFFFFu), acc);
-          acc = __builtin_fmaf(x1.w, bf16_bits_to_f32(w[3] >> 16), acc);
+          acc = chain8(acc, x0, x1, wb[i]);
+          // Reload wb[i] only after its last use: the empty asm makes the
+          // row offset depend on acc, so the scheduler cannot hoist the load
+          // (a hoisted load needs a second register set, copied back behind
+          // a full wait at the loop's back edge).
+          asm("" : "+v"(wrow) : "v"(acc));
+          wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * (nxt + i), 0));
         }
       }
       if (live) lv[tk][slot] = a.router_bias ? acc + a.router_bias[e] : acc;
     }
   };
-  if (npc % 32 == 0)
-    chains(std::integral_constant<int, 32>{});
+  if (npc % 16 == 0)
+    chains(std::integral_constant<int, 16>{});
   else
     chains(std::integral_constant<int, 8>{});
   __syncthreads();
@@ -611,7 +638,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
 namespace {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct RouteWs {
-  size_t hist, wn, alog, xnorm, total;
+  size_t hist, wn, alog, total;
 };
 RouteWs route_ws_layout(int T, int E) {
   const size_t nb = (size_t)(T + kRouteTokens - 1) / kRouteTokens;
@@ -619,8 +646,7 @@ RouteWs route_ws_layout(int T, int E) {
   L.hist = 0;                                                     // per-block expert histograms
   L.wn = align256(nb * (size_t)E * sizeof(int32_t));             // router row norms
   L.alog = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));      // approximate logits [T][E]
-  L.xnorm = L.alog + align256((size_t)T * E * sizeof(float));     // token row norms
-  L.total = L.xnorm + align256((size_t)T * sizeof(float));
+  L.total = L.alog + align256((size_t)T * E * sizeof(float));
   return L;
 }
 }  // namespace
@@ -634,13 +660,13 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   float* wn = reinterpret_cast<float*>(base + L.wn);
   float* alog = reinterpret_cast<float*>(base + L.alog);
-  float* xnorm = reinterpret_cast<float*>(base + L.xnorm);
   hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_logits_kernel, dim3((a.T + kLgTok - 1) / kLgTok), dim3(256), 0, stream, a, alog, xnorm);
+  const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
+  hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb), dim3(256), 0, stream, a, ntb, neb, alog);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select_kernel, dim3(nb), dim3(256), 0, stream, a, alog, xnorm, wn, hist);
+  hipLaunchKernelGGL(route_select_kernel, dim3(nb), dim3(256), 0, stream, a, alog, wn, hist);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, nb, a.T, a.K, a.E,
                      a.has_shared, a.out);
