@@ -24,9 +24,12 @@
  * SwiGLU expert FFN, the gate/up row split and the top-k weighted combine are
  * not on the pages; they are the layer's definition as taken for this build.
  *
- * Precision: router logits in fp32 with a fixed sequential order over the
- * hidden axis (this decides integer expert ids, so both implementations take
- * that decision in the same precision and order); dequantized weights are
+ * Precision: router logits in fp32 with a fixed order over the hidden axis
+ * (blocks of 64 consecutive columns, each summed in column order, the block
+ * sums then added in block order); this decides integer expert ids, so both
+ * implementations take that decision in the same precision and order.  The
+ * pages fix no summation order; this one lets a parallel implementation
+ * give every block of a logit its own lane.  Dequantized weights are
  * bf16 (the pages' matrix-op input format); the expert h activation is
  * rounded to bf16 before the down projection (same reason); every other sum
  * is accumulated in fp64 and rounded once.
@@ -84,8 +87,12 @@ static void set_threads(int nthreads) {
 }
 
 /* ---- step 1: router logits ------------------------------------------------
- * l[t,e] = sum_h x[t,h] * Wr[e,h] (+ rb[e]), fp32, h = 0..H-1 in order.
+ * l[t,e] = sum_h x[t,h] * Wr[e,h] (+ rb[e]) in fp32, in a fixed order:
+ * s_b = the sum over the columns h of block b (64 consecutive columns; the
+ * last block may be shorter) in ascending h, starting from 0; l = the sum of
+ * s_0, s_1, ... in block order, starting from 0; then + rb[e].
  * Each bf16*bf16 product is exact in fp32, so contraction cannot change it. */
+#define MOE_REF_LOGIT_BLOCK 64
 int moe_ref_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
                    const float* rb, float* logits, int nthreads) {
   if (T < 0 || H <= 0 || E <= 0 || (T > 0 && (!x || !wr || !logits))) return -1;
@@ -94,9 +101,14 @@ int moe_ref_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
   for (int t = 0; t < T; ++t) {
     for (int e = 0; e < E; ++e) {
       float acc = 0.0f;
-      for (int h = 0; h < H; ++h) {
-        float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);
-        acc = acc + p;
+      for (int h0 = 0; h0 < H; h0 += MOE_REF_LOGIT_BLOCK) {
+        const int h1 = h0 + MOE_REF_LOGIT_BLOCK < H ? h0 + MOE_REF_LOGIT_BLOCK : H;
+        float sb = 0.0f;
+        for (int h = h0; h < h1; ++h) {
+          float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);
+          sb = sb + p;
+        }
+        acc = acc + sb;
       }
       if (rb) acc = acc + rb[e];
       logits[(size_t)t * E + e] = acc;

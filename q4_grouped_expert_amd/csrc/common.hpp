@@ -20,10 +20,8 @@ constexpr int kWave = 64;
 constexpr int kTileRows = 128;
 // Quant groups per weight row the GEMM keeps in LDS (reduction dim <= 2048).
 constexpr int kMaxGroupsPerRow = 32;
-// Tokens per router workgroup (4 waves x 4 tokens).
-constexpr int kRouteTokens = 16;
-// Hidden-axis chunk staged through LDS by the router.
-constexpr int kRouteChunk = 32;
+// Tokens per expert-histogram group of the router (the scan runs over groups).
+constexpr int kHistTokens = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -50,7 +48,8 @@ struct RouteArgs {
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
 };
-// Routing scratch (per-workgroup expert histograms) and launcher.
+// Routing scratch (expert histograms per 64-token group, router-row norms,
+// approximate logits) and launcher.
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream);
 

@@ -1,8 +1,7 @@
-// Routing kernels: router logits + top-k (one pass over x and the router
-// weight), then histogram -> exclusive scan -> stable scatter -> tile block
-// map, all on the device so the host never waits inside the layer
-// ("Perplexity Lily 오픈소스 공개", alltoptrend.co.kr, section 5-2;
-// "Apple silicon용 Lily, Qwen 추론 최적화", aitrends.kr, section
+// Routing kernels: router logits + top-k, then histogram -> exclusive scan ->
+// stable scatter -> tile block map, all on the device so the host never
+// waits inside the layer ("Perplexity Lily 오픈소스 공개", alltoptrend.co.kr,
+// section 5-2; "Apple silicon용 Lily, Qwen 추론 최적화", aitrends.kr, section
 // "GPU 상주와 메모리 절감").
 #include <math.h>
 
@@ -15,43 +14,59 @@ namespace moeq4 {
 // ---------------------------------------------------------------------------
 // Router logits and top-k.
 //
-// Logit contract: l[t,e] = sum_h x[t,h] * Wr[e,h] in fp32 with h strictly
-// ascending, then + bias[e].  A bf16 x bf16 product is exact in fp32, so an
-// fma chain in that order rounds exactly like "acc = acc + x*w"; every
-// implementation that keeps the order gets bit-identical logits and hence
-// bit-identical expert ids.
+// Logit contract: l[t,e] is an fp32 sum in a fixed order.  The hidden axis
+// splits into blocks of 64 columns; s_b = sum of x[t,h] * Wr[e,h] over block
+// b in ascending h, from 0; l = s_0 + s_1 + ... in block order, from 0; then
+// + bias[e].  A bf16 x bf16 product is exact in fp32, so an fma chain in that
+// order rounds exactly like "s = s + x*w"; every implementation that keeps
+// the order gets bit-identical logits and hence bit-identical expert ids.
 //
-// Computing all T*E chains on the fp32 VALU costs 2*T*H*E flops.  Instead:
+// Computing all T*E logits on the fp32 VALU costs 2*T*H*E flops.  Instead:
 //  1. approximate logits a[t,e] with bf16 MFMA (fp32 accumulation, any
 //     internal order);
 //  2. bound both errors: |a - exact| <= da and |canonical - exact| <= dc,
-//     with sum_h |x w| <= ||x_t|| * max_e ||w_e|| (Cauchy-Schwarz),
+//     with sum_h |x w| <= ||x_t|| * max_e ||w_e|| =: S (Cauchy-Schwarz),
 //     da = 34 (H/32 + 1) 2^-23 S  (each 32-product MFMA step off by at most
 //     33 fp32 ulps of its inputs, for any summation order or truncation),
-//     dc = (H + 2) 2^-24 S  (sequential fp32 summation);
+//     dc = (H + 2) 2^-24 S  (bounds any order of fp32 summation of H terms,
+//     the blocked order included);
 //  3. with tau = the K-th largest a[t,.], every expert outside
 //     {e : a[t,e] >= tau - 2 (da + dc)} has a canonical logit strictly below
 //     the K-th largest canonical logit, so it cannot be selected;
-//  4. recompute the canonical chains for the candidates only (about K+2 per
+//  4. compute the canonical logits of the candidates only (about K+1 per
 //     token) and select the top-k among them exactly.
 // The result equals the full canonical computation, ties included.  When
 // softmax weights run over all E experts (norm_topk = 0) every expert is a
 // candidate.
 // ---------------------------------------------------------------------------
 
-// ||w_e||_2 of every router row, one wave per expert.
-__global__ __launch_bounds__(64) void route_wnorm_kernel(const uint16_t* __restrict__ wr, int H, float* wn) {
+namespace {
+constexpr int kSelTokens = 4;    // tokens per selection workgroup (one wave each)
+constexpr int kLogitBlock = 64;  // columns per block of the canonical logit order
+}  // namespace
+
+// ||w_e||_2 of every router row, one wave per expert; the workgroups also
+// clear the expert histograms that the selection kernel accumulates into.
+__global__ __launch_bounds__(64) void route_wnorm_kernel(const uint16_t* __restrict__ wr, int H, float* wn,
+                                                         int32_t* __restrict__ hist, int hist_len) {
   const int e = blockIdx.x, lane = threadIdx.x;
+  for (int i = e * 64 + lane; i < hist_len; i += gridDim.x * 64) hist[i] = 0;
+  // H <= 2048: at most four 16-byte pieces per lane, all loaded before use
+  u32x4 v[MOE_MAX_REDUCTION / 512];
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
+    const int h = 8 * lane + 512 * i;
+    v[i] = h < H ? *reinterpret_cast<const u32x4*>(wr + (size_t)e * H + h) : u32x4{0u, 0u, 0u, 0u};
+  }
   float s = 0.0f;
-  for (int h = 8 * lane; h < H; h += 512) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(wr + (size_t)e * H + h);
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float lo = bf16_bits_to_f32(v[q] & 0xFFFFu), hi = bf16_bits_to_f32(v[q] >> 16);
+      const float lo = bf16_bits_to_f32(v[i][q] & 0xFFFFu), hi = bf16_bits_to_f32(v[i][q] >> 16);
       s = __builtin_fmaf(lo, lo, s);
       s = __builtin_fmaf(hi, hi, s);
     }
-  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) wn[e] = sqrtf(s);
@@ -76,7 +91,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt has six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-constexpr int kXfPad = 4;    // fp32 padding per staged token row (bank spread)
+// Order-preserving map of an fp32 value to uint32 (-0 is taken as +0 first,
+// so equal values get equal keys) and its inverse.
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Lanes below this one in the wave.
+__device__ __forceinline__ uint64_t lanes_below() {
+  return (1ull << __lane_id()) - 1ull;
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -243,72 +270,86 @@ __device__ __forceinline__ float chain8(float acc, float4 x0, float4 x1, u32x4 w
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Selection: candidates from the approximate logits, canonical fp32 chains
-// for the candidates only, exact top-k and combine weights, and this block's
-// expert histogram.  One workgroup = 16 tokens, 16 lanes per token for the
-// per-token steps; the chains of all 16 tokens are packed one per lane.
+// Selection: candidates from the approximate logits, canonical logits for the
+// candidates only, exact top-k, combine weights, expert histogram.
+//
+// One workgroup = 4 tokens; wave w owns token w in the per-token steps.  The
+// canonical logits of all the workgroup's candidates are spread as pairs of
+// chains over the waves: lane l of a pair computes block l % 32 of chain
+// l / 32 (one block sum, a 64-step fma chain), the block sums meet in LDS
+// and lane 0 of each half adds them in block order.  Token rows sit in LDS
+// as fp32 with each block's 16-byte chunks rotated by the block index, so
+// the 16 lanes of an LDS cycle read 16 different bank groups.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
                                                            const float* __restrict__ wn,
                                                            int32_t* __restrict__ hist) {
-  constexpr int TB = kRouteTokens;  // 16 tokens
-  // token rows in fp32 (padded rows spread the chains' reads over the banks)
-  __shared__ __attribute__((aligned(16))) float xf[TB * (MOE_MAX_REDUCTION + kXfPad)];
-  __shared__ float lv[TB][MOE_MAX_EXPERTS];  // canonical values of the candidates
+  constexpr int TB = kSelTokens;
+  __shared__ __attribute__((aligned(16))) float xf[TB * MOE_MAX_REDUCTION];
+  __shared__ float lv[TB][MOE_MAX_EXPERTS];  // canonical logits of the candidates
   __shared__ short cand[TB][MOE_MAX_EXPERTS];
-  __shared__ int ccount[TB], cstart[TB + 1];
+  __shared__ float part[TB][64];             // block sums of a wave's chain pair
+  __shared__ unsigned long long selk[TB][MOE_MAX_TOPK];
+  __shared__ int ccount[TB];
   __shared__ float wmax_s, xn_s[TB];
   __shared__ int bhist[MOE_MAX_EXPERTS];
+  __shared__ float bias_s[MOE_MAX_EXPERTS];  // router bias (read in the chain loop without a global load)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
   const int T = a.T, H = a.H, E = a.E, K = a.K;
-  const int xstride = H + kXfPad;
+  const int nblk = H / kLogitBlock;
   const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
   const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
+  // fp32 position of column h of token row r in LDS
+  auto xpos = [&](int r, int h) {
+    const int b = h >> 6, q = (h >> 2) & 15;
+    return r * MOE_MAX_REDUCTION + 64 * b + 4 * (q ^ (b & 15));
+  };
 
   bhist[tid] = 0;
-  // ---- token rows to fp32 in LDS, their norms; largest router-row norm ---
-  // 16 lanes per token, 16-byte pieces 128 columns apart; each lane issues
-  // up to 16 loads before it converts any, so a 2048-column row costs one
-  // memory latency.
+  bias_s[tid] = a.router_bias && tid < E ? a.router_bias[tid] : 0.0f;
+  // ---- token row of wave w to fp32 in LDS, its norm; largest router-row norm
   {
-    const int tt = tid >> 4, seg = tid & 15;
-    const bool tv = t0 + tt < T;
+    const int t = t0 + wave;
+    const bool tv = t < T;
+    u32x4 v[MOE_MAX_REDUCTION / 512];
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
+      const int h = 8 * lane + 512 * i;
+      const uint32_t off = tv && h < H ? ((uint32_t)t * H + h) * 2u : kOob;
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+    }
+    float wv[MOE_MAX_EXPERTS / 64];
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < MOE_MAX_EXPERTS / 64; ++i) wv[i] = lane + 64 * i < E ? wn[lane + 64 * i] : 0.0f;
+    }
     float s2 = 0.0f;
-    for (int hb = 0; hb < H; hb += 2048) {
-      u32x4 v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hb + 128 * i + 8 * seg;
-        const uint32_t off = tv && h < H ? (uint32_t)((t0 + tt) * H + h) * 2u : kOob;
-        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
-      }
+    for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
+      const int h = 8 * lane + 512 * i;
+      if (h < H) {
+        float f[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hb + 128 * i + 8 * seg;
-        if (h < H) {
-          float f[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f[2 * q] = bf16_bits_to_f32(v[i][q] & 0xFFFFu);
-            f[2 * q + 1] = bf16_bits_to_f32(v[i][q] >> 16);
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) s2 = __builtin_fmaf(f[q], f[q], s2);
-          float4* dst = reinterpret_cast<float4*>(&xf[tt * xstride + h]);
-          dst[0] = float4{f[0], f[1], f[2], f[3]};
-          dst[1] = float4{f[4], f[5], f[6], f[7]};
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = bf16_bits_to_f32(v[i][q] & 0xFFFFu);
+          f[2 * q + 1] = bf16_bits_to_f32(v[i][q] >> 16);
         }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s2 = __builtin_fmaf(f[q], f[q], s2);
+        *reinterpret_cast<float4*>(&xf[xpos(wave, h)]) = float4{f[0], f[1], f[2], f[3]};
+        *reinterpret_cast<float4*>(&xf[xpos(wave, h + 4)]) = float4{f[4], f[5], f[6], f[7]};
       }
     }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, 16);
-    if (seg == 0) xn_s[tt] = sqrtf(s2);
+    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+    if (lane == 0) xn_s[wave] = sqrtf(s2);
     if (wave == 0) {
       float m = 0.0f;
-      for (int e = lane; e < E; e += 64) m = fmaxf(m, wn[e]);
+#pragma unroll
+      for (int i = 0; i < MOE_MAX_EXPERTS / 64; ++i) m = fmaxf(m, wv[i]);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
       if (lane == 0) wmax_s = m;
@@ -316,204 +357,208 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   }
   __syncthreads();
 
-  // ---- candidates per token (16 lanes per token) ------------------------
-  const int tok = 4 * wave + lg;  // this 16-lane group's token
-  const bool tvalid = t0 + tok < T;
+  // ---- candidates of token w (lane holds experts 4 lane .. 4 lane + 3) ------
+  const int t = t0 + wave;
+  const bool tvalid = t < T;
   {
-    float v[16];
+    float v[4];
+    uint32_t key[4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = 16 * ln + q;
-      v[q] = (tvalid && e < E) ? alog[(size_t)(t0 + tok) * E + e] : -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      v[j] = tvalid && e < E ? alog[(size_t)t * E + e] : -INFINITY;
+      key[j] = tvalid && e < E ? fkey(v[j]) : 0u;
     }
-    uint32_t taken = 0;
-    float tau = -INFINITY;
-    for (int k = 0; k < K; ++k) {
-      float bv = -INFINITY;
-      int bq = -1;
+    // tau = the K-th largest approximate logit: the largest th with at least
+    // K keys >= th, built bit by bit (wave-uniform)
+    uint32_t th = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = th | (1u << bit);
+      int n = 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (!((taken >> q) & 1u) && (bq < 0 || v[q] > bv)) {
-          bv = v[q];
-          bq = q;
-        }
-      float gv = bv;
-      int gl = bq >= 0 ? ln : 16;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(gv, o, 16);
-        const int ol = __shfl_xor(gl, o, 16);
-        if (ov > gv || (ov == gv && ol < gl)) {
-          gv = ov;
-          gl = ol;
-        }
-      }
-      if (gl == ln && bq >= 0) taken |= 1u << bq;
-      tau = gv;
+      for (int j = 0; j < 4; ++j) n += __popcll(__ballot(key[j] >= c));
+      if (n >= K) th = c;
     }
+    const float tau = fkey_inv(th);
     float win;
     if (!a.norm_topk) {
       win = INFINITY;
     } else {
-      const float S = xn_s[tok] * wmax_s * 1.001f;
+      const float S = xn_s[wave] * wmax_s * 1.001f;
       const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
       const float dc = (float)(H + 2) * 0x1p-24f * S;
       win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
     }
-    uint32_t m = 0;
+    // compact the candidates in expert order
+    bool f[4];
+    uint64_t bal[4];
+    int below = 0, total = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (16 * ln + q < E && v[q] >= tau - win) m |= 1u << q;
-    const int cnt = __popc(m);
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int u = __shfl_up(incl, o, 16);
-      if (ln >= o) incl += u;
+    for (int j = 0; j < 4; ++j) {
+      f[j] = tvalid && 4 * lane + j < E && v[j] >= tau - win;
+      bal[j] = __ballot(f[j]);
+      below += __popcll(bal[j] & lanes_below());
+      total += __popcll(bal[j]);
     }
-    int pos = incl - cnt;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if ((m >> q) & 1u) cand[tok][pos++] = (short)(16 * ln + q);
-    if (ln == 15) ccount[tok] = tvalid ? incl : 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < TB; ++t) {
-      cstart[t] = run;
-      run += ccount[t];
-    }
-    cstart[TB] = run;
+    for (int j = 0; j < 4; ++j)
+      if (f[j]) cand[wave][below++] = (short)(4 * lane + j);
+    if (lane == 0) ccount[wave] = total;
   }
   __syncthreads();
 
-  // ---- canonical chains: l = sum_h x[t,h] w[e,h] in fp32, h ascending ------
-  // Chain c of the block's list runs on thread c % 256 (batch c / 256); the
-  // router row streams from L2 in 16-byte pieces P pieces ahead (P = 16, or
-  // 8 where H is not a multiple of 128, since the unrolled body walks whole
-  // groups of P pieces), the token row comes from LDS.  bf16 x bf16
-  // products are exact in fp32, so each fma rounds exactly like
-  // "acc = acc + x*w".
-  const int npc = H / 8;
-  auto chains = [&](auto depth) {
-    constexpr int P = decltype(depth)::value;
-    const int total = cstart[TB];
-    for (int c = tid; c < ((total + 255) / 256) * 256; c += 256) {
-      const bool live = c < total;
+  // ---- canonical logits of all candidates, two chains per wave pass ------
+  {
+    int cst[TB + 1];
+    cst[0] = 0;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) cst[i + 1] = cst[i] + ccount[i];
+    const int nchain = cst[TB];
+    const int npair = (nchain + 1) / 2;
+    const int half = lane >> 5, b = lane & 31;
+    // chain c -> (token slot, expert); row offset of this lane's block, or
+    // an offset that reads zeros
+    auto locate = [&](int c, int& tk, int& slot, int& e) {
+      tk = 0;
+#pragma unroll
+      for (int i = 1; i < TB; ++i) tk += c >= cst[i] ? 1 : 0;
+      slot = c - cst[tk];
+      e = cand[tk][slot];
+    };
+    auto row_off = [&](int p) -> uint32_t {
+      const int c = 2 * p + half;
+      if (p >= npair || c >= nchain || b >= nblk) return kOob;
+      int tk, slot, e;
+      locate(c, tk, slot, e);
+      return ((uint32_t)e * H + kLogitBlock * b) * 2u;
+    };
+    auto load = [&](u32x4 (&w)[8], uint32_t off) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, off, 16 * i, 0));
+    };
+    // block sum of pair p from the loaded router piece w; returns it so a
+    // reload can be made to depend on it
+    auto block_sum = [&](const u32x4 (&w)[8], int p) -> float {
+      const int c = 2 * p + half;
       int tk = 0;
 #pragma unroll
-      for (int t = 1; t < TB; ++t) tk += (live && c >= cstart[t]) ? 1 : 0;
-      const int slot = c - cstart[tk];
-      const int e = live ? cand[tk][slot] : 0;
-      uint32_t wrow = live ? (uint32_t)e * H * 2u : kOob;
-      const float* xr = &xf[tk * xstride];
-      // first group in piece order (the loop's waits assume wb[i] was issued
-      // i-th, on entry as on the back edge)
-      u32x4 wb[P];
+      for (int i = 1; i < TB; ++i) tk += c >= cst[i] ? 1 : 0;
+      float sb = 0.0f;
+      const float* xr = &xf[tk * MOE_MAX_REDUCTION + kLogitBlock * b];
+      const int sw = b & 15;
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * i, 0));
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 8; ++i) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&xr[4 * ((2 * i) ^ sw)]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&xr[4 * ((2 * i + 1) ^ sw)]);
+        sb = chain8(sb, x0, x1, w[i]);
       }
-      float acc = 0.0f;
-      for (int p0 = 0; p0 < npc; p0 += P) {
-        const int nxt = p0 + P < npc ? p0 + P : p0;  // the last group re-reads itself
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-          const float4 x0 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i)]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i) + 4]);
-          acc = chain8(acc, x0, x1, wb[i]);
-          // Reload wb[i] only after its last use: the empty asm makes the
-          // row offset depend on acc, so the scheduler cannot hoist the load
-          // (a hoisted load needs a second register set, copied back behind
-          // a full wait at the loop's back edge).
-          asm("" : "+v"(wrow) : "v"(acc));
-          wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, wrow, 16 * (nxt + i), 0));
-        }
+      return sb;
+    };
+    // block sums -> LDS -> lane 0 of each half adds them in block order
+    auto finish = [&](float sb, int p) {
+      part[wave][lane] = sb;
+      __builtin_amdgcn_wave_barrier();
+      const int c = 2 * p + half;
+      if (b == 0 && c < nchain) {
+        int tk, slot, e;
+        locate(c, tk, slot, e);
+        float acc = 0.0f;
+        for (int i = 0; i < nblk; ++i) acc = acc + part[wave][32 * half + i];
+        if (a.router_bias) acc = acc + bias_s[e];
+        lv[tk][slot] = acc;
       }
-      if (live) lv[tk][slot] = a.router_bias ? acc + a.router_bias[e] : acc;
-    }
-  };
-  if (npc % 16 == 0)
-    chains(std::integral_constant<int, 16>{});
-  else
-    chains(std::integral_constant<int, 8>{});
-  __syncthreads();
-  const int C = ccount[tok];
-
-  // ---- exact top-k among the candidates ----------------------------------
-  if (tvalid) {
-    const int t = t0 + tok;
-    uint32_t taken = 0;  // bit r: candidate ln + 16 r taken
-    float sel_v[MOE_MAX_TOPK];
-    int sel_e[MOE_MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      sel_v[k] = 0.0f;
-      sel_e[k] = 0;
-      if (k < K) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff, br = -1;
-        for (int r = 0; ln + 16 * r < C; ++r) {
-          if ((taken >> r) & 1u) continue;
-          const int cc = ln + 16 * r;
-          const float vv = lv[tok][cc];
-          const int ee = cand[tok][cc];
-          if (br < 0 || vv > bv || (vv == bv && ee < be)) {
-            bv = vv;
-            be = ee;
-            br = r;
-          }
-        }
-        float gv = bv;
-        int ge = br >= 0 ? be : 0x7fffffff;
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-          const float ov = __shfl_xor(gv, o, 16);
-          const int oe = __shfl_xor(ge, o, 16);
-          if (oe != 0x7fffffff && (ov > gv || (ov == gv && oe < ge) || ge == 0x7fffffff)) {
-            gv = ov;
-            ge = oe;
-          }
-        }
-        if (br >= 0 && be == ge) taken |= 1u << br;
-        sel_v[k] = gv;
-        sel_e[k] = ge;
-      }
-    }
-    const float mx = sel_v[0];
-    float den = 0.0f;
-    if (a.norm_topk) {
-#pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k)
-        if (k < K) den += expf(sel_v[k] - mx);
-    } else {
-      float s = 0.0f;
-      for (int cc = ln; cc < C; cc += 16) s += expf(lv[tok][cc] - mx);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
-      den = s;
-    }
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      if (k < K && ln == k) {
-        a.out.topk_ids[(size_t)t * K + k] = sel_e[k];
-        a.out.topk_w[(size_t)t * K + k] = expf(sel_v[k] - mx) / den;
-        atomicAdd(&bhist[sel_e[k]], 1);
+      __builtin_amdgcn_wave_barrier();
+    };
+    u32x4 wa[8], wb[8];
+    uint32_t offa = row_off(wave);
+    load(wa, offa);
+    for (int p = wave; p < npair; p += 2 * TB) {
+      uint32_t offb = row_off(p + TB);
+      load(wb, offb);
+      const float sa = block_sum(wa, p);
+      // the reload of wa must follow its last use (else a second register
+      // set and a full wait at the back edge): tie its offset to sa
+      offa = row_off(p + 2 * TB);
+      asm("" : "+v"(offa) : "v"(sa));
+      load(wa, offa);
+      finish(sa, p);
+      if (p + TB < npair) {
+        const float sb2 = block_sum(wb, p + TB);
+        finish(sb2, p + TB);
       }
     }
   }
   __syncthreads();
-  if (tid < E) hist[(size_t)blockIdx.x * E + tid] = bhist[tid];
+
+  // ---- exact top-k of token w among its candidates -----------------------
+  if (tvalid) {
+    const int C = ccount[wave];
+    // composite keys: value, then lower expert first (E <= 256)
+    unsigned long long ck[MOE_MAX_EXPERTS / 64];
+#pragma unroll
+    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
+      const int c = lane + 64 * r;
+      ck[r] = c < C ? ((unsigned long long)fkey(lv[wave][c]) << 8) | (unsigned)(255 - cand[wave][c]) : 0ull;
+    }
+    unsigned long long th = 0;
+    for (int bit = 39; bit >= 0; --bit) {
+      const unsigned long long c = th | (1ull << bit);
+      int n = 0;
+#pragma unroll
+      for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) n += __popcll(__ballot(ck[r] >= c));
+      if (n >= K) th = c;
+    }
+    // exactly K keys are >= th (keys are distinct); gather them
+    int below = 0;
+#pragma unroll
+    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
+      const bool s = ck[r] >= th && ck[r] != 0ull;
+      const uint64_t bal = __ballot(s);
+      const int pos = below + __popcll(bal & lanes_below());
+      if (s) selk[wave][pos] = ck[r];
+      below += __popcll(bal);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float mx = -INFINITY;
+    unsigned long long mine = 0;
+    int rank = 0;
+    for (int k = 0; k < K; ++k) {
+      const unsigned long long o = selk[wave][k];
+      mx = fmaxf(mx, fkey_inv((uint32_t)(o >> 8)));
+      if (lane == k) mine = o;
+    }
+    if (lane < K)
+      for (int k = 0; k < K; ++k) rank += selk[wave][k] > mine ? 1 : 0;
+    float den = 0.0f;
+    if (a.norm_topk) {
+      for (int k = 0; k < K; ++k) den += expf(fkey_inv((uint32_t)(selk[wave][k] >> 8)) - mx);
+    } else {
+      float s = 0.0f;
+      for (int c = lane; c < C; c += 64) s += expf(lv[wave][c] - mx);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      den = s;
+    }
+    if (lane < K) {
+      const int e = 255 - (int)(mine & 255ull);
+      const float v = fkey_inv((uint32_t)(mine >> 8));
+      a.out.topk_ids[(size_t)t * K + rank] = e;
+      a.out.topk_w[(size_t)t * K + rank] = expf(v - mx) / den;
+      atomicAdd(&bhist[e], 1);
+    }
+  }
+  __syncthreads();
+  // this workgroup's tokens lie in one histogram group of kHistTokens
+  if (tid < E && bhist[tid]) atomicAdd(&hist[(size_t)(t0 / kHistTokens) * E + tid], bhist[tid]);
 }
 
 // ---------------------------------------------------------------------------
 // Exclusive scan of the expert histogram and the tile block map.
 //
-// hist[b][e] holds router workgroup b's count for expert e; it is rewritten
-// in place into the exclusive prefix over b (the rows of e that earlier
-// workgroups own), counts[e] is the total, offsets the exclusive scan over e
+// hist[g][e] holds the rows of expert e among the tokens of group g (64
+// tokens each); it is rewritten in place into the exclusive prefix over g
+// (the rows of e that earlier groups own), counts[e] is the total, offsets the exclusive scan over e
 // and the block map lists each expert's tiles of at most kTileRows rows, then
 // the shared expert's.  One workgroup, one lane per expert.
 // ---------------------------------------------------------------------------
@@ -596,20 +641,20 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_scan_kernel(int32_t* __
 }
 
 // ---------------------------------------------------------------------------
-// Stable scatter.  Router workgroup b's tokens land at
-//   offsets[e] + (rows of e owned by workgroups < b) + (rank inside b),
-// the rank being the number of earlier tokens of the same 16-token block that
-// chose e (a 16-bit LDS mask per expert; a token's experts are distinct).
+// Stable scatter: sorted_idx / inv_pos.  One workgroup per histogram group of
+// 64 tokens, one lane per token; a (t, k) row's place inside its expert group
+// is the rows of that expert in earlier groups (the scanned histogram) plus
+// the group's earlier tokens that chose the same expert (a 64-bit LDS mask).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ hist, int T, int K, int E,
                                                            moe_route_out out) {
-  __shared__ uint32_t mask[MOE_MAX_EXPERTS];
+  __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
   const int lane = threadIdx.x;
-  const int b = blockIdx.x;
-  for (int e = lane; e < E; e += 64) mask[e] = 0u;
+  const int g = blockIdx.x;
+  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
   __syncthreads();
-  const int t = b * kRouteTokens + lane;
-  const bool valid = lane < kRouteTokens && t < T;
+  const int t = g * kHistTokens + lane;
+  const bool valid = t < T;
   int my[MOE_MAX_TOPK];
 #pragma unroll
   for (int k = 0; k < MOE_MAX_TOPK; ++k) {
@@ -617,7 +662,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
     if (valid && k < K) {
       const int e = out.topk_ids[(size_t)t * K + k];
       my[k] = (unsigned)e < (unsigned)E ? e : 0;  // ids are produced in range; clamp keeps indexing safe
-      atomicOr(&mask[my[k]], 1u << lane);
+      atomicOr(&mask[my[k]], 1ull << lane);
     }
   }
   __syncthreads();
@@ -626,8 +671,8 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
     for (int k = 0; k < MOE_MAX_TOPK; ++k) {
       if (k < K) {
         const int e = my[k];
-        const int rank = __popc(mask[e] & ((1u << lane) - 1u));
-        const int p = out.offsets[e] + hist[(size_t)b * E + e] + rank;
+        const int rank = __popcll(mask[e] & lanes_below());
+        const int p = out.offsets[e] + hist[(size_t)g * E + e] + rank;
         out.sorted_idx[p] = t * K + k;
         out.inv_pos[(size_t)t * K + k] = p;
       }
@@ -641,10 +686,10 @@ struct RouteWs {
   size_t hist, wn, alog, total;
 };
 RouteWs route_ws_layout(int T, int E) {
-  const size_t nb = (size_t)(T + kRouteTokens - 1) / kRouteTokens;
+  const size_t ng = (size_t)(T + kHistTokens - 1) / kHistTokens;
   RouteWs L;
-  L.hist = 0;                                                     // per-block expert histograms
-  L.wn = align256(nb * (size_t)E * sizeof(int32_t));             // router row norms
+  L.hist = 0;                                                     // expert histograms per 64-token group
+  L.wn = align256(ng * (size_t)E * sizeof(int32_t));             // router row norms
   L.alog = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));      // approximate logits [T][E]
   L.total = L.alog + align256((size_t)T * E * sizeof(float));
   return L;
@@ -654,24 +699,25 @@ RouteWs route_ws_layout(int T, int E) {
 size_t route_workspace_bytes(int T, int E) { return route_ws_layout(T, E).total; }
 
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
-  const int nb = (a.T + kRouteTokens - 1) / kRouteTokens;
+  const int ng = (a.T + kHistTokens - 1) / kHistTokens;
   const RouteWs L = route_ws_layout(a.T, a.E);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   float* wn = reinterpret_cast<float*>(base + L.wn);
   float* alog = reinterpret_cast<float*>(base + L.alog);
-  hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn);
+  hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn, hist, ng * a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
   hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb), dim3(256), 0, stream, a, ntb, neb, alog);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select_kernel, dim3(nb), dim3(256), 0, stream, a, alog, wn, hist);
+  hipLaunchKernelGGL(route_select_kernel, dim3((a.T + kSelTokens - 1) / kSelTokens), dim3(256), 0, stream, a, alog,
+                     wn, hist);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, nb, a.T, a.K, a.E,
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ng, a.T, a.K, a.E,
                      a.has_shared, a.out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(64), 0, stream, hist, a.T, a.K, a.E, a.out);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(ng), dim3(64), 0, stream, hist, a.T, a.K, a.E, a.out);
   return hipGetLastError();
 }
 

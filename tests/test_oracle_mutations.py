@@ -26,7 +26,14 @@ MUTATIONS = {
     "unstable scatter": ("int p = cursor[ids[r]]++;",
                          "int p = offsets[ids[r]+1] - 1 - (cursor[ids[r]]++ - offsets[ids[r]]);"),
     "weights not renormalized": ("if (norm_topk) {", "if (!norm_topk) {"),
-    "logit sum reversed": ("for (int h = 0; h < H; ++h) {\n        float p", "for (int h = H - 1; h >= 0; --h) {\n        float p"),
+    "logit sum reversed inside a block": ("for (int h = h0; h < h1; ++h) {", "for (int h = h1 - 1; h >= h0; --h) {"),
+    "logit as one chain over all columns": ("          sb = sb + p;\n        }\n        acc = acc + sb;\n",
+                                            "          acc = acc + p;\n        }\n"),
+    "logit block sums added in reverse": (
+        "for (int h0 = 0; h0 < H; h0 += MOE_REF_LOGIT_BLOCK) {",
+        "for (int h0 = (H - 1) / MOE_REF_LOGIT_BLOCK * MOE_REF_LOGIT_BLOCK; h0 >= 0; h0 -= MOE_REF_LOGIT_BLOCK) {"),
+    "logit block of 32 columns": ("#define MOE_REF_LOGIT_BLOCK 64", "#define MOE_REF_LOGIT_BLOCK 32"),
+    "logit block of 128 columns": ("#define MOE_REF_LOGIT_BLOCK 64", "#define MOE_REF_LOGIT_BLOCK 128"),
     "row token index wrong": ("row_token[r] = sorted_idx[offsets[e] + r] / K;",
                               "row_token[r] = sorted_idx[offsets[e] + r] % T;"),
 }
