@@ -138,10 +138,11 @@ int moe_route_block_rows(void);
 int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 
 /* Workspace bytes needed by moe_route (ws_kind = 0: expert histograms per
- * 64-token group, ceil(T/64) * E int32, 256 fp32 router-row norms and the
- * approximate router logits T * E fp32, each piece 256-byte aligned) or
- * moe_layer_forward (ws_kind = 1; also routing buffers, h and y).  Host-only, pure.  Workspace contents need
- * no initialization and are overwritten. */
+ * 64-token group, E * (ceil(T/64) rounded up to 4) int32, 256 fp32
+ * router-row norms and the approximate router logits T * E fp32, each piece
+ * 256-byte aligned) or moe_layer_forward (ws_kind = 1; also routing
+ * buffers, h and y).  Host-only, pure.  Workspace contents need no
+ * initialization and are overwritten. */
 int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes);
 
 /* Routing, steps histogram -> scan -> scatter -> block map included.

@@ -91,6 +91,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt has six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt lgkmcnt(0) alone (vmcnt 63 and expcnt 7 leave those counters
+// unconstrained).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
 // Order-preserving map of an fp32 value to uint32 (-0 is taken as +0 first,
 // so equal values get equal keys) and its inverse.
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -283,13 +286,16 @@ __device__ __forceinline__ float chain8(float acc, float4 x0, float4 x1, u32x4 w
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
                                                            const float* __restrict__ wn,
-                                                           int32_t* __restrict__ hist) {
+                                                           int32_t* __restrict__ hist, int ngp) {
   constexpr int TB = kSelTokens;
   __shared__ __attribute__((aligned(16))) float xf[TB * MOE_MAX_REDUCTION];
-  __shared__ float lv[TB][MOE_MAX_EXPERTS];  // canonical logits of the candidates
+  // canonical logits of the candidates as keys: fkey(logit) << 8 | 255 - e
+  // (larger key = larger logit, then lower expert; E <= 256)
+  __shared__ unsigned long long ck[TB][MOE_MAX_EXPERTS];
   __shared__ short cand[TB][MOE_MAX_EXPERTS];
-  __shared__ float part[TB][64];             // block sums of a wave's chain pair
-  __shared__ unsigned long long selk[TB][MOE_MAX_TOPK];
+  // block sums of a wave's last (up to) 4 chain pairs, [pair % 4][lane]
+  __shared__ __attribute__((aligned(16))) float part[TB][4][64];
+  __shared__ float selv[TB][MOE_MAX_TOPK];
   __shared__ int ccount[TB];
   __shared__ float wmax_s, xn_s[TB];
   __shared__ int bhist[MOE_MAX_EXPERTS];
@@ -310,10 +316,19 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 
   bhist[tid] = 0;
   bias_s[tid] = a.router_bias && tid < E ? a.router_bias[tid] : 0.0f;
+  const int t = t0 + wave;
+  const bool tvalid = t < T;
+  // approximate logits of token w, lane holding experts 4 lane .. 4 lane + 3
+  // (loaded now so their latency overlaps the token row's)
+  float av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    av[j] = tvalid && e < E ? alog[(size_t)t * E + e] : 0.0f;
+  }
   // ---- token row of wave w to fp32 in LDS, its norm; largest router-row norm
   {
-    const int t = t0 + wave;
-    const bool tv = t < T;
+    const bool tv = tvalid;
     u32x4 v[MOE_MAX_REDUCTION / 512];
 #pragma unroll
     for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
@@ -357,29 +372,25 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   }
   __syncthreads();
 
-  // ---- candidates of token w (lane holds experts 4 lane .. 4 lane + 3) ------
-  const int t = t0 + wave;
-  const bool tvalid = t < T;
+  // ---- candidates of token w ---------------------------------------------
   {
-    float v[4];
+    const float* v = av;
     uint32_t key[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * lane + j;
-      v[j] = tvalid && e < E ? alog[(size_t)t * E + e] : -INFINITY;
-      key[j] = tvalid && e < E ? fkey(v[j]) : 0u;
-    }
-    // tau = the K-th largest approximate logit: the largest th with at least
-    // K keys >= th, built bit by bit (wave-uniform)
+    for (int j = 0; j < 4; ++j) key[j] = tvalid && 4 * lane + j < E ? fkey(v[j]) >> 16 : 0u;
+    // tau <= the K-th largest approximate logit: th = the largest 16-bit key
+    // prefix with at least K keys at or above it, built bit by bit
+    // (wave-uniform); th << 16 is at most the K-th largest key, and a lower
+    // tau only widens the candidate set
     uint32_t th = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 15; bit >= 0; --bit) {
       const uint32_t c = th | (1u << bit);
       int n = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) n += __popcll(__ballot(key[j] >= c));
       if (n >= K) th = c;
     }
-    const float tau = fkey_inv(th);
+    const float tau = fkey_inv(th << 16);
     float win;
     if (!a.norm_topk) {
       win = INFINITY;
@@ -437,8 +448,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
       for (int i = 0; i < 8; ++i)
         w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, off, 16 * i, 0));
     };
-    // block sum of pair p from the loaded router piece w; returns it so a
-    // reload can be made to depend on it
+    // block sum of pair p from this lane's router block w
     auto block_sum = [&](const u32x4 (&w)[8], int p) -> float {
       const int c = 2 * p + half;
       int tk = 0;
@@ -455,24 +465,41 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
       }
       return sb;
     };
-    // block sums -> LDS -> lane 0 of each half adds them in block order
-    auto finish = [&](float sb, int p) {
-      part[wave][lane] = sb;
+    // Block sums go to LDS, one row of 64 per pair; after every 4th pair of
+    // the wave (and after its last) lane j < 8 adds the block sums of chain
+    // j of those pairs in block order, so the 32-add chains of 8 chains run
+    // side by side.  p0 is the wave's first pair of the batch, n its size.
+    auto combine = [&](int p0, int n) {
       __builtin_amdgcn_wave_barrier();
-      const int c = 2 * p + half;
-      if (b == 0 && c < nchain) {
+      const int j = lane;          // chain 2 (p0 + TB (j / 2)) + j % 2
+      const int pj = p0 + TB * (j >> 1);
+      const int c = 2 * pj + (j & 1);
+      if (j < 2 * n && c < nchain) {
         int tk, slot, e;
         locate(c, tk, slot, e);
+        const float* row = &part[wave][j >> 1][32 * (j & 1)];
+        float ps[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 q = *reinterpret_cast<const float4*>(&row[4 * i]);
+          ps[4 * i] = q.x;
+          ps[4 * i + 1] = q.y;
+          ps[4 * i + 2] = q.z;
+          ps[4 * i + 3] = q.w;
+        }
         float acc = 0.0f;
-        for (int i = 0; i < nblk; ++i) acc = acc + part[wave][32 * half + i];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (i < nblk) acc = acc + ps[i];
         if (a.router_bias) acc = acc + bias_s[e];
-        lv[tk][slot] = acc;
+        ck[tk][slot] = ((unsigned long long)fkey(acc) << 8) | (unsigned)(255 - e);
       }
       __builtin_amdgcn_wave_barrier();
     };
     u32x4 wa[8], wb[8];
     uint32_t offa = row_off(wave);
     load(wa, offa);
+    int it = 0;  // pairs of this wave so far
     for (int p = wave; p < npair; p += 2 * TB) {
       uint32_t offb = row_off(p + TB);
       load(wb, offb);
@@ -482,115 +509,116 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
       offa = row_off(p + 2 * TB);
       asm("" : "+v"(offa) : "v"(sa));
       load(wa, offa);
-      finish(sa, p);
+      part[wave][it & 3][lane] = sa;
+      ++it;
       if (p + TB < npair) {
-        const float sb2 = block_sum(wb, p + TB);
-        finish(sb2, p + TB);
+        part[wave][it & 3][lane] = block_sum(wb, p + TB);
+        ++it;
       }
+      if ((it & 3) == 0) combine(wave + TB * (it - 4), 4);
     }
+    if (it & 3) combine(wave + TB * (it & ~3), it & 3);
   }
   __syncthreads();
 
   // ---- exact top-k of token w among its candidates -----------------------
+  // A candidate's slot is the number of its token's candidates with a larger
+  // key (keys are distinct); the K smallest slots are the selection, already
+  // in slot order.
   if (tvalid) {
     const int C = ccount[wave];
-    // composite keys: value, then lower expert first (E <= 256)
-    unsigned long long ck[MOE_MAX_EXPERTS / 64];
+    const unsigned long long* kw = ck[wave];
+    unsigned long long mine[MOE_MAX_EXPERTS / 64];
+    int rank[MOE_MAX_EXPERTS / 64];
 #pragma unroll
     for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
       const int c = lane + 64 * r;
-      ck[r] = c < C ? ((unsigned long long)fkey(lv[wave][c]) << 8) | (unsigned)(255 - cand[wave][c]) : 0ull;
-    }
-    unsigned long long th = 0;
-    for (int bit = 39; bit >= 0; --bit) {
-      const unsigned long long c = th | (1ull << bit);
-      int n = 0;
-#pragma unroll
-      for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) n += __popcll(__ballot(ck[r] >= c));
-      if (n >= K) th = c;
-    }
-    // exactly K keys are >= th (keys are distinct); gather them
-    int below = 0;
-#pragma unroll
-    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
-      const bool s = ck[r] >= th && ck[r] != 0ull;
-      const uint64_t bal = __ballot(s);
-      const int pos = below + __popcll(bal & lanes_below());
-      if (s) selk[wave][pos] = ck[r];
-      below += __popcll(bal);
+      mine[r] = c < C ? kw[c] : 0ull;
+      rank[r] = C;
+      if (64 * r < C) {
+        int n = 0;
+#pragma unroll 4
+        for (int o = 0; o < C; ++o) n += kw[o] > mine[r] ? 1 : 0;
+        rank[r] = n;
+        if (c < C && n < K) selv[wave][n] = fkey_inv((uint32_t)(mine[r] >> 8));
+      }
     }
     __builtin_amdgcn_wave_barrier();
-    float mx = -INFINITY;
-    unsigned long long mine = 0;
-    int rank = 0;
-    for (int k = 0; k < K; ++k) {
-      const unsigned long long o = selk[wave][k];
-      mx = fmaxf(mx, fkey_inv((uint32_t)(o >> 8)));
-      if (lane == k) mine = o;
-    }
-    if (lane < K)
-      for (int k = 0; k < K; ++k) rank += selk[wave][k] > mine ? 1 : 0;
+    const float mx = selv[wave][0];
     float den = 0.0f;
     if (a.norm_topk) {
-      for (int k = 0; k < K; ++k) den += expf(fkey_inv((uint32_t)(selk[wave][k] >> 8)) - mx);
+      for (int k = 0; k < K; ++k) den += expf(selv[wave][k] - mx);
     } else {
-      float s = 0.0f;
-      for (int c = lane; c < C; c += 64) s += expf(lv[wave][c] - mx);
+      float sum = 0.0f;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      den = s;
+      for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r)
+        if (lane + 64 * r < C) sum += expf(fkey_inv((uint32_t)(mine[r] >> 8)) - mx);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      den = sum;
     }
-    if (lane < K) {
-      const int e = 255 - (int)(mine & 255ull);
-      const float v = fkey_inv((uint32_t)(mine >> 8));
-      a.out.topk_ids[(size_t)t * K + rank] = e;
-      a.out.topk_w[(size_t)t * K + rank] = expf(v - mx) / den;
-      atomicAdd(&bhist[e], 1);
+#pragma unroll
+    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
+      if (lane + 64 * r < C && rank[r] < K) {
+        const int e = 255 - (int)(mine[r] & 255ull);
+        a.out.topk_ids[(size_t)t * K + rank[r]] = e;
+        a.out.topk_w[(size_t)t * K + rank[r]] = expf(selv[wave][rank[r]] - mx) / den;
+        atomicAdd(&bhist[e], 1);
+      }
     }
   }
   __syncthreads();
-  // this workgroup's tokens lie in one histogram group of kHistTokens
-  if (tid < E && bhist[tid]) atomicAdd(&hist[(size_t)(t0 / kHistTokens) * E + tid], bhist[tid]);
+  // this workgroup's tokens lie in one histogram group of kHistTokens;
+  // hist is [E][ngp]
+  if (tid < E && bhist[tid]) atomicAdd(&hist[(size_t)tid * ngp + t0 / kHistTokens], bhist[tid]);
 }
 
 // ---------------------------------------------------------------------------
-// Exclusive scan of the expert histogram and the tile block map.
+// Group offsets, tile block map and stable scatter (sorted_idx / inv_pos).
 //
-// hist[g][e] holds the rows of expert e among the tokens of group g (64
-// tokens each); it is rewritten in place into the exclusive prefix over g
-// (the rows of e that earlier groups own), counts[e] is the total, offsets the exclusive scan over e
-// and the block map lists each expert's tiles of at most kTileRows rows, then
-// the shared expert's.  One workgroup, one lane per expert.
+// hist[e][g] holds the rows of expert e among the tokens of group g (64
+// tokens each); rows are ngp = ng rounded up to 4 ints long.  One workgroup per group, one thread per expert: it sums its
+// expert's row of hist into the total count and the rows that earlier groups
+// own, a workgroup-wide exclusive scan of the totals gives the expert group
+// offsets, and the first wave places the group's rows: a (t, k) row goes to
+// offsets[e] + (rows of e in earlier groups) + (earlier tokens of this group
+// that chose e, from a 64-bit LDS mask).  Workgroup 0 also writes counts,
+// offsets and the block map (each expert's tiles of at most kTileRows rows,
+// then the shared expert's).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_scan_kernel(int32_t* __restrict__ hist, int nblk, int T,
-                                                                     int K, int E, int has_shared,
-                                                                     moe_route_out out) {
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int32_t* __restrict__ hist, int ngp,
+                                                                      int T, int K, int E, int has_shared,
+                                                                      moe_route_out out) {
   __shared__ int wsum[MOE_MAX_EXPERTS / 64][2];
+  __shared__ int before_s[MOE_MAX_EXPERTS], off_s[MOE_MAX_EXPERTS];
+  __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
+  const int g = blockIdx.x;
   constexpr int BM = kTileRows;
 
-  int run = 0;
+  mask[e] = 0ull;
+  // per-expert total and the part owned by groups before g; a row of hist
+  // (ngp ints, 16-byte aligned, zero past ng) is read 64 groups per round,
+  // all loads of a round in flight together
+  int run = 0, before = 0;
   if (e < E) {
-    int b = 0;
-    for (; b + 8 <= nblk; b += 8) {
-      int v[8];
+    const int4* row = reinterpret_cast<const int4*>(hist + (size_t)e * ngp);
+    for (int g0 = 0; g0 < ngp; g0 += 64) {
+      int4 v[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = hist[(size_t)(b + i) * E + e];
+      for (int i = 0; i < 16; ++i) v[i] = g0 + 4 * i < ngp ? row[g0 / 4 + i] : int4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hist[(size_t)(b + i) * E + e] = run;
-        run += v[i];
+      for (int i = 0; i < 16; ++i) {
+        const int gi = g0 + 4 * i;
+        before += (gi < g ? v[i].x : 0) + (gi + 1 < g ? v[i].y : 0) + (gi + 2 < g ? v[i].z : 0) +
+                  (gi + 3 < g ? v[i].w : 0);
+        run += v[i].x + v[i].y + v[i].z + v[i].w;
       }
-    }
-    for (; b < nblk; ++b) {
-      const int v = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
-      run += v;
     }
   }
   const int nt = (run + BM - 1) / BM;
-  // block-wide exclusive scans of counts and tile counts
+  // workgroup-wide exclusive scans of counts and tile counts
   int ic = run, it = nt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -612,56 +640,46 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_scan_kernel(int32_t* __
   }
   const int off = bc + ic - run;
   const int tst = bt + it - nt;
-  if (e < E) {
-    out.counts[e] = run;
-    out.offsets[e] = off;
-    for (int i = 0; i < nt; ++i) {
-      int32_t* bm = out.block_map + 4 * (tst + i);
-      bm[0] = e;
-      bm[1] = off + i * BM;
-      bm[2] = min(BM, run - i * BM);
-      bm[3] = 0;
+  before_s[e] = before;
+  off_s[e] = off;
+  if (g == 0) {
+    if (e < E) {
+      out.counts[e] = run;
+      out.offsets[e] = off;
+      for (int i = 0; i < nt; ++i) {
+        int32_t* bm = out.block_map + 4 * (tst + i);
+        bm[0] = e;
+        bm[1] = off + i * BM;
+        bm[2] = min(BM, run - i * BM);
+        bm[3] = 0;
+      }
+    }
+    if (e == MOE_MAX_EXPERTS - 1) {
+      // totals over all lanes (lanes >= E contribute 0)
+      const int R = bc + ic;
+      const int tiles = bt + it;
+      const int nsh = has_shared ? (T + BM - 1) / BM : 0;
+      out.offsets[E] = R;
+      *out.n_tiles = tiles + nsh;
+      for (int i = 0; i < nsh; ++i) {
+        int32_t* bm = out.block_map + 4 * (tiles + i);
+        bm[0] = E;
+        bm[1] = R + i * BM;
+        bm[2] = min(BM, T - i * BM);
+        bm[3] = 0;
+      }
     }
   }
-  if (e == MOE_MAX_EXPERTS - 1) {
-    // totals over all lanes (lanes >= E contribute 0)
-    const int R = bc + ic;
-    const int tiles = bt + it;
-    const int nsh = has_shared ? (T + BM - 1) / BM : 0;
-    out.offsets[E] = R;
-    *out.n_tiles = tiles + nsh;
-    for (int i = 0; i < nsh; ++i) {
-      int32_t* bm = out.block_map + 4 * (tiles + i);
-      bm[0] = E;
-      bm[1] = R + i * BM;
-      bm[2] = min(BM, T - i * BM);
-      bm[3] = 0;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Stable scatter: sorted_idx / inv_pos.  One workgroup per histogram group of
-// 64 tokens, one lane per token; a (t, k) row's place inside its expert group
-// is the rows of that expert in earlier groups (the scanned histogram) plus
-// the group's earlier tokens that chose the same expert (a 64-bit LDS mask).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ hist, int T, int K, int E,
-                                                           moe_route_out out) {
-  __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
-  const int lane = threadIdx.x;
-  const int g = blockIdx.x;
-  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
-  __syncthreads();
+  // ---- scatter of this group's rows (first wave, one lane per token) ------
   const int t = g * kHistTokens + lane;
-  const bool valid = t < T;
+  const bool valid = wave == 0 && t < T;
   int my[MOE_MAX_TOPK];
 #pragma unroll
   for (int k = 0; k < MOE_MAX_TOPK; ++k) {
     my[k] = 0;
     if (valid && k < K) {
-      const int e = out.topk_ids[(size_t)t * K + k];
-      my[k] = (unsigned)e < (unsigned)E ? e : 0;  // ids are produced in range; clamp keeps indexing safe
+      const int id = out.topk_ids[(size_t)t * K + k];
+      my[k] = (unsigned)id < (unsigned)E ? id : 0;  // ids are produced in range; clamp keeps indexing safe
       atomicOr(&mask[my[k]], 1ull << lane);
     }
   }
@@ -670,9 +688,9 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k) {
       if (k < K) {
-        const int e = my[k];
-        const int rank = __popcll(mask[e] & lanes_below());
-        const int p = out.offsets[e] + hist[(size_t)g * E + e] + rank;
+        const int x = my[k];
+        const int rank = __popcll(mask[x] & lanes_below());
+        const int p = off_s[x] + before_s[x] + rank;
         out.sorted_idx[p] = t * K + k;
         out.inv_pos[(size_t)t * K + k] = p;
       }
@@ -685,10 +703,12 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct RouteWs {
   size_t hist, wn, alog, total;
 };
+// expert-histogram row length: 64-token groups rounded up to 4
+int hist_row(int T) { return ((T + kHistTokens - 1) / kHistTokens + 3) & ~3; }
 RouteWs route_ws_layout(int T, int E) {
-  const size_t ng = (size_t)(T + kHistTokens - 1) / kHistTokens;
+  const size_t ng = (size_t)hist_row(T);
   RouteWs L;
-  L.hist = 0;                                                     // expert histograms per 64-token group
+  L.hist = 0;                                                     // expert histograms [E][64-token groups]
   L.wn = align256(ng * (size_t)E * sizeof(int32_t));             // router row norms
   L.alog = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));      // approximate logits [T][E]
   L.total = L.alog + align256((size_t)T * E * sizeof(float));
@@ -699,25 +719,23 @@ RouteWs route_ws_layout(int T, int E) {
 size_t route_workspace_bytes(int T, int E) { return route_ws_layout(T, E).total; }
 
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
-  const int ng = (a.T + kHistTokens - 1) / kHistTokens;
+  const int ng = (a.T + kHistTokens - 1) / kHistTokens, ngp = hist_row(a.T);
   const RouteWs L = route_ws_layout(a.T, a.E);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   float* wn = reinterpret_cast<float*>(base + L.wn);
   float* alog = reinterpret_cast<float*>(base + L.alog);
-  hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn, hist, ng * a.E);
+  hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn, hist, ngp * a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
   hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb), dim3(256), 0, stream, a, ntb, neb, alog);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_select_kernel, dim3((a.T + kSelTokens - 1) / kSelTokens), dim3(256), 0, stream, a, alog,
-                     wn, hist);
+                     wn, hist, ngp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ng, a.T, a.K, a.E,
+  hipLaunchKernelGGL(route_group_kernel, dim3(ng), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ngp, a.T, a.K, a.E,
                      a.has_shared, a.out);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(ng), dim3(64), 0, stream, hist, a.T, a.K, a.E, a.out);
   return hipGetLastError();
 }
 
