@@ -17,7 +17,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Rows per GEMM tile in the block map.
-constexpr int kTileRows = 128;
+constexpr int kTileRows = 256;
 // Quant groups per weight row the GEMM keeps in LDS (reduction dim <= 2048).
 constexpr int kMaxGroupsPerRow = 32;
 // Tokens per expert-histogram group of the router (the scan runs over groups).

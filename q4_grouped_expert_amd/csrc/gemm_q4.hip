@@ -9,32 +9,37 @@
 //    (80 KB of LDS and at most 256 registers per wave each), so every SIMD
 //    runs two independent waves: while one issues MFMAs the other dequantizes,
 //    waits at its barrier or runs its prologue/epilogue.
-//  * A workgroup computes one block-map tile (<= 128 rows of one expert
-//    group) against a 256-column slice of that expert's weights (gate/up:
-//    128 gate + the matching 128 up columns).  Each wave owns every row of the
-//    tile and 64 weight columns (four 16-column MFMA subtiles): every weight of
-//    the slice is dequantized by exactly one lane, the accumulators (<= 128
-//    per lane) sit in AGPRs, and each activation fragment read from LDS feeds
-//    4 MFMAs.
-//  * The number of live 16-row subtiles (1..8) is a template parameter,
-//    picked once per workgroup: a 70-row group runs a 5-subtile body with
+//  * A workgroup computes one block-map tile (<= 256 rows of one expert
+//    group) against a 128-column slice of that expert's weights (gate/up:
+//    64 gate + the matching 64 up columns).  Each wave owns every row of the
+//    tile and 32 weight columns (two 16-column MFMA subtiles): every weight
+//    of the slice is dequantized by exactly one lane per tile, and a tile
+//    holds a whole expert group of up to 256 rows, so an expert's weights
+//    are streamed and dequantized once per column slice whatever its row
+//    count; the accumulators (<= 128 per lane) stay in registers.
+//  * The number of live 16-row subtiles (1..16) is a template parameter,
+//    picked once per workgroup: a 150-row group runs a 10-subtile body with
 //    straight-line code and no MFMAs beyond the last partial subtile.
 //  * Activations (x rows gathered through sorted_idx, or h rows) reach LDS by
-//    direct-to-LDS buffer loads into a 3-slot ring of 64-column stages (one
-//    quant group each), issued two stages ahead of use, with a 16-byte-chunk
-//    XOR swizzle that keeps MFMA fragment reads conflict-free.
+//    direct-to-LDS buffer loads into a 2-slot ring of 64-column stages (one
+//    quant group each), issued one stage ahead and spread over the MFMA
+//    regions, with a 16-byte-chunk XOR swizzle that keeps MFMA fragment
+//    reads conflict-free.
 //  * Weights go from global memory straight to VGPRs through buffer loads
-//    (per-lane row offset in a VGPR, stage offset in an SGPR), three stages
+//    (per-lane row offset in a VGPR, stage offset in an SGPR), two stages
 //    ahead of use: a lane loads 8 bytes = 16 codes of one weight row, forms
 //    q*scale+bias with one fma per weight in fp32, rounds to bf16 and feeds
-//    the result as the B operand of v_mfma_f32_16x16x32_bf16; accumulation
-//    is fp32.  The tile's scales and biases for the whole reduction are
-//    loaded once per tile into LDS tables.
+//    the result as the A operand of v_mfma_f32_16x16x32_bf16 (activations
+//    are the B operand, so each lane ends with 4 consecutive output columns
+//    of one row); accumulation is fp32.  The tile's scales and biases for the
+//    whole reduction are loaded once per tile into LDS tables.
 //  * The reduction index is permuted identically for A and B inside each
 //    64-wide group (lane group g, MFMA step s -> columns 16g+8s..16g+8s+7),
 //    which lets one 8-byte code load serve both MFMA steps.
 //  * Gate/up mode gives each wave gate rows j and up rows I+j for the same
-//    32 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers.
+//    16 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers
+//    and leaves as one 8-byte store per row and subtile; down writes fp32 y
+//    with one 16-byte store per row and subtile.
 //  * Block order: tiles are visited largest first (the block map lists the
 //    shared expert's full tiles last, so it is walked backwards) and the
 //    N-slices of one tile get workgroup ids that are equal modulo 8, which
@@ -51,11 +56,11 @@ namespace moeq4 {
 
 namespace {
 
-constexpr int BM = kTileRows;    // max rows per tile (128 = 8 MFMA subtiles)
+constexpr int BM = kTileRows;    // max rows per tile (256 = 16 MFMA subtiles)
 constexpr int BK = 64;           // reduction columns per stage (= quant group)
 constexpr int NWAVES = 4;        // one wave per SIMD
 constexpr int NT = 64 * NWAVES;  // lanes per workgroup
-constexpr int NS = 4;            // 16-column subtiles per wave
+constexpr int NS = 2;            // 16-column subtiles per wave
 constexpr int WN = 16 * NS;      // columns per wave
 constexpr int BN = NWAVES * WN;  // weight columns per workgroup
 constexpr int kXcds = 8;
@@ -119,10 +124,18 @@ struct TileCtx {
   bool jval[NS];
 };
 
+// s_waitcnt that bounds only the vector-memory counter (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool kGateUp, int MSUB>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* __restrict__ A0,
-                                          uint16_t* __restrict__ A1, uint16_t* __restrict__ A2,
-                                          uint16_t* __restrict__ Ssh, uint16_t* __restrict__ Bsh) {
+                                          uint16_t* __restrict__ A1, uint16_t* __restrict__ Ssh,
+                                          uint16_t* __restrict__ Bsh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int Kd = g.Kdim;
@@ -152,7 +165,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   }
 
   f32x4 acc[MSUB][NS];  // first written by the k-step-0 MFMAs of stage 0
-  BRegs bq[3];          // codes of three consecutive stages
+  BRegs bq[2];          // codes of two consecutive stages
   bf16x8 bf[NS][2];     // dequantized B fragments of the current stage
 
   auto dma_a = [&](uint16_t* slot, int kt) {
@@ -161,17 +174,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           t.a_rs, (__attribute__((address_space(3))) void*)(slot + (ROWS_PER_DMA * i + 8 * wave) * BK), 16, adoff[i],
           kt * BK * 2, 0, 0);
-  };
-  // Wait until this wave's DMA writes into `slot` have landed: a dummy LDS
-  // read inside every region the wave's DMAs wrote makes the compiler insert
-  // the vmcnt wait for the last of them (it tracks direct-to-LDS loads per
-  // address range, so one read would only wait for the DMA that covers it).
-  auto wait_slot = [&](const uint16_t* slot) {
-#pragma unroll
-    for (int i = 0; i < ADMA; ++i) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(slot + (ROWS_PER_DMA * i + 8 * wave) * BK + 2 * lane);
-      asm volatile("" ::"v"(v));
-    }
   };
   auto load_b = [&](BRegs& q, int kt) {
 #pragma unroll
@@ -217,91 +219,109 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   };
 
   // Every wave issues the same, unconditional sequence of loads (stage
-  // indices clamped at the end, rows past the group reading zeros), so the
-  // compiler can count outstanding loads exactly and wait only for the ones
-  // a stage needs.
+  // indices clamped at the end, rows past the group reading zeros): per
+  // stage ADMA direct-to-LDS loads then NS code loads, and no other vector
+  // memory access, so the wait before each barrier can count them.
   const int nk = t.nk;
   const int last = nk - 1;
   dma_sb();
   dma_a(A0, 0);
   load_b(bq[0], 0);
-  dma_a(A1, min(1, last));
   load_b(bq[1], min(1, last));
-  load_b(bq[2], min(2, last));
   __syncthreads();  // every wave's DMAs of the tables and of stage 0 landed
   dequant(bq[0], 0);
 
-  // Stage kt (ring slot kt%3, codes bq[kt%3]):
-  //  - DMA stage kt+2 into the slot read in stage kt-1 (free since the last
-  //    barrier) and load the codes of stage kt+3 into bq[kt%3] (dequantized
-  //    at the end of stage kt-1);
+  // Stage kt (ring slot kt%2, codes bq[kt%2]):
+  //  - DMA stage kt+1 into the other slot (read in stage kt-1, free since the
+  //    last barrier) and load the codes of stage kt+2 into bq[kt%2]
+  //    (dequantized at the end of stage kt-1);
   //  - per 16-row subtile m, one scheduling region with the LDS reads of
-  //    subtile m+1's A fragments and subtile m's 8 MFMAs;
+  //    subtile m+2's A fragments and subtile m's 2*NS MFMAs;
   //  - dequantize stage kt+1's codes into bf in place (the MFMAs have read
-  //    their operands), wait for this wave's DMA of stage kt+1 and meet at
-  //    the barrier (a plain s_barrier: a fenced one would drain every
-  //    outstanding load).
-  auto stage = [&](auto first, int kt, BRegs& qown, const BRegs& qnext, const uint16_t* Ab,
-                   uint16_t* Anext, uint16_t* Afree) {
-    dma_a(Afree, min(kt + 2, last));
-    load_b(qown, min(kt + 3, last));
-    bf16x8 af[2][2];
-    af[0][0] = a_frag(Ab, 0, 0);
-    af[0][1] = a_frag(Ab, 0, 1);
+  //    their operands), wait until only this stage's NS code loads are in
+  //    flight (so the DMA of stage kt+1 has landed) and meet at the barrier
+  //    (a plain s_barrier: a fenced one would drain every outstanding load).
+  auto stage = [&](auto first, int kt, BRegs& qown, const BRegs& qnext, const uint16_t* Ab, uint16_t* Anext) {
+    // The loads for later stages are spread over the subtile regions (DMA i
+    // in region i, the code loads in the region after the last DMA), so
+    // their issue overlaps this wave's MFMAs; the DMAs still come first.
+    const int ka = min(kt + 1, last);
+    auto dma_one = [&](int i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          t.a_rs, (__attribute__((address_space(3))) void*)(Anext + (ROWS_PER_DMA * i + 8 * wave) * BK), 16, adoff[i],
+          ka * BK * 2, 0, 0);
+    };
+    // A fragments are read two subtiles ahead of their MFMAs (a subtile's
+    // 2*NS MFMAs alone are shorter than an LDS read)
+    bf16x8 af[3][2];
+#pragma unroll
+    for (int m = 0; m < 2 && m < MSUB; ++m) {
+      af[m][0] = a_frag(Ab, m, 0);
+      af[m][1] = a_frag(Ab, m, 1);
+    }
 #pragma unroll
     for (int m = 0; m < MSUB; ++m) {
-      if (m + 1 < MSUB) {
-        af[(m + 1) & 1][0] = a_frag(Ab, m + 1, 0);
-        af[(m + 1) & 1][1] = a_frag(Ab, m + 1, 1);
+      if (m + 2 < MSUB) {
+        af[(m + 2) % 3][0] = a_frag(Ab, m + 2, 0);
+        af[(m + 2) % 3][1] = a_frag(Ab, m + 2, 1);
       }
+      if (m < ADMA) dma_one(m);
+      if (m == ADMA) load_b(qown, min(kt + 2, last));
+      // weights as the A operand, activations as B: the 16x16 result holds
+      // output row 16m + ln, columns 4*lg..4*lg+3 of subtile j in each lane
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        if constexpr (decltype(first)::value) mfma_first(acc[m][j], af[m & 1][0], bf[j][0]);
-        else mfma_acc(acc[m][j], af[m & 1][0], bf[j][0]);
+        if constexpr (decltype(first)::value) mfma_first(acc[m][j], bf[j][0], af[m % 3][0]);
+        else mfma_acc(acc[m][j], bf[j][0], af[m % 3][0]);
       }
 #pragma unroll
-      for (int j = 0; j < NS; ++j) mfma_acc(acc[m][j], af[m & 1][1], bf[j][1]);
+      for (int j = 0; j < NS; ++j) mfma_acc(acc[m][j], bf[j][1], af[m % 3][1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (ADMA >= MSUB) load_b(qown, min(kt + 2, last));
     // the last stage dequantizes its own codes again (clamped), unused
     dequant(qnext, min(kt + 1, last));
-    wait_slot(Anext);
+    wait_vmcnt<NS>();
     __builtin_amdgcn_s_barrier();
   };
   const std::integral_constant<bool, true> kFirst;
   const std::integral_constant<bool, false> kNext;
 
-  // Stage 0 starts the accumulators; then three stages per iteration with no
-  // conditions inside, so the wait counts at the loop head are exact; the
-  // last (nk - 1) % 3 stages follow the loop.
-  stage(kFirst, 0, bq[0], bq[1], A0, A1, A2);
+  // Stage 0 starts the accumulators; then two stages per iteration with no
+  // conditions inside; the last (nk - 1) % 2 stage follows the loop.
+  stage(kFirst, 0, bq[0], bq[1], A0, A1);
   int kt = 1;
-  for (; kt + 3 <= nk; kt += 3) {
-    stage(kNext, kt, bq[1], bq[2], A1, A2, A0);
-    stage(kNext, kt + 1, bq[2], bq[0], A2, A0, A1);
-    stage(kNext, kt + 2, bq[0], bq[1], A0, A1, A2);
+  for (; kt + 2 <= nk; kt += 2) {
+    stage(kNext, kt, bq[1], bq[0], A1, A0);
+    stage(kNext, kt + 1, bq[0], bq[1], A0, A1);
   }
-  if (kt < nk) stage(kNext, kt, bq[1], bq[2], A1, A2, A0);
-  if (kt + 1 < nk) stage(kNext, kt + 1, bq[2], bq[0], A2, A0, A1);
+  if (kt < nk) stage(kNext, kt, bq[1], bq[0], A1, A0);
+  wait_vmcnt<0>();  // no direct-to-LDS write outlives the tile
 
-  // ---- epilogue: MFMA 16x16 output layout, lane holds rows 4*lg+i, column ln
+  // ---- epilogue: lane holds output row 16m + ln, columns 4*lg..4*lg+3 of
+  // each subtile, written as one vector store per subtile
+  const int r_in = ln;
   if (kGateUp) {
-    // subtiles 0,1: gate columns; 2,3: the matching up columns
+    // subtile 0: gate columns; 1: the matching up columns
     uint16_t* h = reinterpret_cast<uint16_t*>(g.c);
+    if (t.jval[0]) {
+      const int c0 = t.ocol[0] - ln + 4 * lg;
 #pragma unroll
-    for (int j = 0; j < NS / 2; ++j) {
-      if (t.jval[j]) {
+      for (int m = 0; m < MSUB; ++m) {
+        const int r = m * 16 + r_in;
+        if (r < t.nrows) {
+          uint32_t hv[2];
 #pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
+          for (int i = 0; i < 2; ++i) {
+            float o[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + 4 * lg + i;
-            if (r < t.nrows) {
-              const float gv = acc[m][j][i], uv = acc[m][j + NS / 2][i];
-              const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-              h[(size_t)(t.row0 + r) * g.I + t.ocol[j]] = f32_to_bf16_bits(gv * sig * uv);
+            for (int q = 0; q < 2; ++q) {
+              const float gv = acc[m][0][2 * i + q], uv = acc[m][1][2 * i + q];
+              o[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             }
+            hv[i] = pack_bf16x2(o[0], o[1]);
           }
+          *reinterpret_cast<u32x2*>(&h[(size_t)(t.row0 + r) * g.I + c0]) = u32x2{hv[0], hv[1]};
         }
       }
     }
@@ -309,14 +329,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     float* y = reinterpret_cast<float*>(g.c);
 #pragma unroll
     for (int m = 0; m < MSUB; ++m) {
+      const int r = m * 16 + r_in;
+      if (r < t.nrows) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + 4 * lg + i;
-        if (r < t.nrows) {
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-            if (t.jval[j]) y[(size_t)(t.row0 + r) * g.N + t.ocol[j]] = acc[m][j][i];
-        }
+        for (int j = 0; j < NS; ++j)
+          if (t.jval[j])
+            *reinterpret_cast<f32x4*>(&y[(size_t)(t.row0 + r) * g.N + t.ocol[j] - ln + 4 * lg]) = acc[m][j];
       }
     }
   }
@@ -324,12 +342,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
 
 template <bool kGateUp>
 __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
-  // activation ring: three stages of [128 rows][64] bf16 (separate objects so
-  // the compiler tracks the direct-to-LDS loads of each slot on its own)
+  // activation ring: two stages of [256 rows][64] bf16
   __shared__ __attribute__((aligned(16))) uint16_t A0[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t A1[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t A2[BM * BK];
-  // the tile's scales and biases: [256 weight rows][<= 32 groups] bf16 each
+  // the tile's scales and biases: [128 weight rows][<= 32 groups] bf16 each
   __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kMaxGroups];
   __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kMaxGroups];
 
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   // This lane's weight rows (one per 16-column subtile).  Subtiles past the
   // matrix edge read row 0 and are never stored.
   if (kGateUp) {
-    // subtiles 0,1: gate rows hc..hc+31; subtiles 2,3: the matching up rows
+    // subtile 0: gate rows hc..hc+15; subtile 1: the matching up rows
     // I + hc..  (hc = this wave's first gate row)
     const int hc = nb * (BN / 2) + wave * (WN / 2);
 #pragma unroll
@@ -389,7 +405,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
       t.ocol[j] = row + ln;
       const uint32_t r = v ? (j < NS / 2 ? 0 : g.I) + row + ln : 0;
       t.c_off[j] = r * cpr + 8u * lg;
-      // scale/bias tables: rows 0..127 = gate rows nb*128.., 128..255 = up rows
+      // scale/bias tables: rows 0..63 = gate rows nb*64.., 64..127 = up rows
       t.sb_row[j] = (j < NS / 2 ? 0 : BN / 2) + wave * (WN / 2) + 16 * jj + ln;
     }
     t.sb_half = (BN / 2) * gpr * 2 / 16;
@@ -405,7 +421,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
       t.c_off[j] = r * cpr + 8u * lg;
       t.sb_row[j] = wave * WN + 16 * j + ln;
     }
-    // one contiguous range of 256 rows, split in two halves of 128
+    // one contiguous range of 128 rows, split in two halves of 64
     t.sb_half = (BN / 2) * gpr * 2 / 16;
     t.sb_src[0] = (uint32_t)(nb * BN) * gpr * 2u;
     t.sb_src[1] = (uint32_t)(nb * BN + BN / 2) * gpr * 2u;
@@ -413,14 +429,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
 
   const int msub = (t.nrows + 15) >> 4;
   switch (msub) {
-    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, A2, Ssh, Bsh); break;
-    default: tile_body<kGateUp, 8>(g, t, A0, A1, A2, Ssh, Bsh); break;
+    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, Ssh, Bsh); break;
+    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, Ssh, Bsh); break;
+    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, Ssh, Bsh); break;
+    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, Ssh, Bsh); break;
+    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, Ssh, Bsh); break;
+    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, Ssh, Bsh); break;
+    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, Ssh, Bsh); break;
+    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, Ssh, Bsh); break;
+    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, Ssh, Bsh); break;
+    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, Ssh, Bsh); break;
+    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, Ssh, Bsh); break;
+    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, Ssh, Bsh); break;
+    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, Ssh, Bsh); break;
+    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, Ssh, Bsh); break;
+    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, Ssh, Bsh); break;
+    default: tile_body<kGateUp, 16>(g, t, A0, A1, Ssh, Bsh); break;
   }
 }
 
