@@ -118,6 +118,8 @@ struct TileCtx {
   int sb_row[NS];       // this lane's rows in the LDS scale/bias tables
   uint32_t sb_src[2];   // byte offsets of the (up to two) contiguous row ranges
   int sb_half;          // 16-byte chunks per range
+  int sb_mask;          // chunk rotation mask of a table row (0: none)
+  int sb_f[NS];         // rotation of this lane's table rows
   int nk;               // stages
   int row0, nrows;
   int ocol[NS];
@@ -185,7 +187,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   auto dequant = [&](const BRegs& q, int kt) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int idx = t.sb_row[j] * gpr + kt;
+      const int idx = t.sb_row[j] * gpr + 8 * ((kt >> 3) ^ t.sb_f[j]) + (kt & 7);
       const float sv = bf16_bits_to_f32(Ssh[idx]), bv = bf16_bits_to_f32(Bsh[idx]);
       bf[j][0] = dequant8(q.c[j][0], sv, bv);
       bf[j][1] = dequant8(q.c[j][1], sv, bv);
@@ -195,7 +197,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   // contiguous row ranges per table, fetched once as whole cache lines with
   // 16-byte direct-to-LDS loads (chunk q of range r lands at LDS byte
   // 16*(r*half + q)).  Chunks past a range read zeros into the slack of the
-  // table.
+  // table.  Inside a table row the 16-byte chunks are rotated by
+  // f(row) = (row * gpr / 128) & mask, so that the 16 consecutive rows one
+  // dequant read touches fall on 16 different bank groups (without it, 32
+  // groups per row put them on 4).
   auto dma_sb = [&]() {
     const int chunks = 2 * t.sb_half;  // both ranges
 #pragma unroll
@@ -204,7 +209,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
       if (q0 < chunks) {
         const int q = q0 + lane;
         const int r = q >= t.sb_half;
-        const int qi = q - r * t.sb_half;
+        int qi = q - r * t.sb_half;
+        if (t.sb_mask) {
+          const int cp = q & t.sb_mask;        // physical chunk in its table row
+          const int row = q / (t.sb_mask + 1);  // table row
+          qi += (cp ^ (((row * gpr) >> 7) & t.sb_mask)) - cp;
+        }
         const uint32_t off = (q < chunks) ? t.sb_src[r] + 16u * qi : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(t.s_rs, (__attribute__((address_space(3))) void*)(Ssh + 8 * q0), 16, off,
                                                  0, 0, 0);
@@ -425,6 +435,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
     t.sb_half = (BN / 2) * gpr * 2 / 16;
     t.sb_src[0] = (uint32_t)(nb * BN) * gpr * 2u;
     t.sb_src[1] = (uint32_t)(nb * BN + BN / 2) * gpr * 2u;
+  }
+
+  {
+    const int cpr8 = (int)gpr / 8;  // 16-byte chunks per table row
+    t.sb_mask = (cpr8 >= 2 && (cpr8 & (cpr8 - 1)) == 0) ? cpr8 - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) t.sb_f[j] = ((t.sb_row[j] * (int)gpr) >> 7) & t.sb_mask;
   }
 
   const int msub = (t.nrows + 15) >> 4;
