@@ -138,7 +138,8 @@ template <bool kGateUp, int MSUB>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* __restrict__ A0,
                                           uint16_t* __restrict__ A1, uint16_t* __restrict__ Ssh,
                                           uint16_t* __restrict__ Bsh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
   const int ln = lane & 15, lg = lane >> 4;
   const int Kd = g.Kdim;
   const int gpr = Kd / 64;  // quant groups per weight row
