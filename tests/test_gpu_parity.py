@@ -53,6 +53,12 @@ SMALL = {
     "E40": gen.custom_shape(130, 256, 128, 40, 6, seed=26),
     "no_shared": gen.custom_shape(90, 256, 192, 16, 4, shared=False, seed=27),
     "tall_group": gen.custom_shape(700, 128, 64, 4, 2, seed=28),
+    # 16 and 32 quant groups per weight row in both GEMMs (the scale/bias
+    # tables' chunk rotation with masks 1 and 3)
+    "H1024_I1024": gen.custom_shape(96, 1024, 1024, 16, 4, seed=33),
+    "H2048_I2048": gen.custom_shape(40, 2048, 2048, 8, 2, seed=34),
+    # an expert count that is not a multiple of 4 (router lanes past E)
+    "E10_K3": gen.custom_shape(45, 256, 128, 10, 3, seed=35),
 }
 
 
