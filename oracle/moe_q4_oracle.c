@@ -24,12 +24,11 @@
  * SwiGLU expert FFN, the gate/up row split and the top-k weighted combine are
  * not on the pages; they are the layer's definition as taken for this build.
  *
- * Precision: router logits in fp32 with a fixed order over the hidden axis
- * (blocks of 64 consecutive columns, each summed in column order, the block
- * sums then added in block order); this decides integer expert ids, so both
- * implementations take that decision in the same precision and order.  The
- * pages fix no summation order; this one lets a parallel implementation
- * give every block of a logit its own lane.  Dequantized weights are
+ * Precision: router logits in fp32, summed over the hidden axis one column
+ * at a time in ascending order (the plain loop); this decides integer expert
+ * ids, so both implementations take that decision in the same precision and
+ * order.  The pages fix no summation order; the plain sequential one is the
+ * reading taken.  Dequantized weights are
  * bf16 (the pages' matrix-op input format); the expert h activation is
  * rounded to bf16 before the down projection (same reason); every other sum
  * is accumulated in fp64 and rounded once.
@@ -87,12 +86,9 @@ static void set_threads(int nthreads) {
 }
 
 /* ---- step 1: router logits ------------------------------------------------
- * l[t,e] = sum_h x[t,h] * Wr[e,h] (+ rb[e]) in fp32, in a fixed order:
- * s_b = the sum over the columns h of block b (64 consecutive columns; the
- * last block may be shorter) in ascending h, starting from 0; l = the sum of
- * s_0, s_1, ... in block order, starting from 0; then + rb[e].
+ * l[t,e] = sum_h x[t,h] * Wr[e,h] (+ rb[e]) in fp32: acc starts at 0, adds
+ * the products for h = 0, 1, ..., H-1 in that order, then adds rb[e].
  * Each bf16*bf16 product is exact in fp32, so contraction cannot change it. */
-#define MOE_REF_LOGIT_BLOCK 64
 int moe_ref_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
                    const float* rb, float* logits, int nthreads) {
   if (T < 0 || H <= 0 || E <= 0 || (T > 0 && (!x || !wr || !logits))) return -1;
@@ -101,14 +97,9 @@ int moe_ref_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
   for (int t = 0; t < T; ++t) {
     for (int e = 0; e < E; ++e) {
       float acc = 0.0f;
-      for (int h0 = 0; h0 < H; h0 += MOE_REF_LOGIT_BLOCK) {
-        const int h1 = h0 + MOE_REF_LOGIT_BLOCK < H ? h0 + MOE_REF_LOGIT_BLOCK : H;
-        float sb = 0.0f;
-        for (int h = h0; h < h1; ++h) {
-          float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);
-          sb = sb + p;
-        }
-        acc = acc + sb;
+      for (int h = 0; h < H; ++h) {
+        float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);
+        acc = acc + p;
       }
       if (rb) acc = acc + rb[e];
       logits[(size_t)t * E + e] = acc;

@@ -26,14 +26,16 @@ MUTATIONS = {
     "unstable scatter": ("int p = cursor[ids[r]]++;",
                          "int p = offsets[ids[r]+1] - 1 - (cursor[ids[r]]++ - offsets[ids[r]]);"),
     "weights not renormalized": ("if (norm_topk) {", "if (!norm_topk) {"),
-    "logit sum reversed inside a block": ("for (int h = h0; h < h1; ++h) {", "for (int h = h1 - 1; h >= h0; --h) {"),
-    "logit as one chain over all columns": ("          sb = sb + p;\n        }\n        acc = acc + sb;\n",
-                                            "          acc = acc + p;\n        }\n"),
-    "logit block sums added in reverse": (
-        "for (int h0 = 0; h0 < H; h0 += MOE_REF_LOGIT_BLOCK) {",
-        "for (int h0 = (H - 1) / MOE_REF_LOGIT_BLOCK * MOE_REF_LOGIT_BLOCK; h0 >= 0; h0 -= MOE_REF_LOGIT_BLOCK) {"),
-    "logit block of 32 columns": ("#define MOE_REF_LOGIT_BLOCK 64", "#define MOE_REF_LOGIT_BLOCK 32"),
-    "logit block of 128 columns": ("#define MOE_REF_LOGIT_BLOCK 64", "#define MOE_REF_LOGIT_BLOCK 128"),
+    "logit sum reversed": ("for (int h = 0; h < H; ++h) {\n        float p", "for (int h = H - 1; h >= 0; --h) {\n        float p"),
+    "logit summed in 64-column blocks": (
+        "      float acc = 0.0f;\n      for (int h = 0; h < H; ++h) {\n"
+        "        float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);\n"
+        "        acc = acc + p;\n      }\n",
+        "      float acc = 0.0f, blk = 0.0f;\n      for (int h = 0; h < H; ++h) {\n"
+        "        float p = bf16_to_f32(x[(size_t)t * H + h]) * bf16_to_f32(wr[(size_t)e * H + h]);\n"
+        "        blk = blk + p;\n        if (h % 64 == 63 || h == H - 1) { acc = acc + blk; blk = 0.0f; }\n      }\n"),
+    "logit accumulated in fp64": ("      float acc = 0.0f;\n      for (int h = 0; h < H; ++h) {",
+                                  "      double acc = 0.0;\n      for (int h = 0; h < H; ++h) {"),
     "row token index wrong": ("row_token[r] = sorted_idx[offsets[e] + r] / K;",
                               "row_token[r] = sorted_idx[offsets[e] + r] % T;"),
 }

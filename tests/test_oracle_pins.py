@@ -106,9 +106,9 @@ def _spike_row(H, cols, vals):
     return bf16_bits(r)
 
 
-def test_logits_order_inside_a_block_exact():
-    # products 1, 2^-24, 2^-24 in one block: left-to-right fp32 gives 1 (each
-    # add is a tie to even); any other order or fp64 gives 1 + 2^-23
+def test_logits_sequential_order_exact():
+    # products 1, 2^-24, 2^-24: left-to-right fp32 gives 1 (each add is a tie
+    # to even); any other order or fp64 gives 1 + 2^-23
     x = bf16_bits(np.float32([[1.0, 2.0 ** -12, 2.0 ** -12]]))
     wr = bf16_bits(np.float32([[1.0, 2.0 ** -12, 2.0 ** -12]]))
     l = oracle.logits(x, wr)
@@ -116,25 +116,20 @@ def test_logits_order_inside_a_block_exact():
     wr2 = bf16_bits(np.float32([[2.0 ** -12, 2.0 ** -12, 1.0]]))
     x2 = bf16_bits(np.float32([[2.0 ** -12, 2.0 ** -12, 1.0]]))
     assert oracle.logits(x2, wr2)[0, 0] == np.float32(1.0 + 2.0 ** -23)
-    # the same three products at columns 0, 62, 63 (block 0 of 64): still 1
-    x3 = _spike_row(128, [0, 62, 63], [1.0, 2.0 ** -12, 2.0 ** -12])
-    assert oracle.logits(x3, x3)[0, 0] == np.float32(1.0)
 
 
-def test_logits_block_sums_exact():
-    # products 1 at column 0 and 2^-24 at columns 64, 65: the second block sums
-    # to 2^-23 exactly and 1 + 2^-23 is representable, while one left-to-right
-    # chain over all columns gives 1
+def test_logits_one_chain_over_all_columns_exact():
+    # the same products far apart stay one left-to-right chain: 1 at column 0
+    # and 2^-24 at columns 64 and 65 give 1 (summing columns 64.. on their own
+    # first would give 2^-23 and then 1 + 2^-23)
     x = _spike_row(128, [0, 64, 65], [1.0, 2.0 ** -12, 2.0 ** -12])
-    assert oracle.logits(x, x)[0, 0] == np.float32(1.0 + 2.0 ** -23)
-    # block sums 1, 2^-24, 2^-24 (columns 0, 64, 128) are added left to right:
-    # 1, whereas adding the two small block sums first gives 1 + 2^-23
-    x = _spike_row(192, [0, 64, 128], [1.0, 2.0 ** -12, 2.0 ** -12])
     assert oracle.logits(x, x)[0, 0] == np.float32(1.0)
+    x = _spike_row(2048, [0, 1000, 2047], [1.0, 2.0 ** -12, 2.0 ** -12])
+    assert oracle.logits(x, x)[0, 0] == np.float32(1.0)
+    # small terms first: 2^-24 + 2^-24 = 2^-23 exactly, then + 1
     x = _spike_row(192, [0, 64, 128], [2.0 ** -12, 2.0 ** -12, 1.0])
     assert oracle.logits(x, x)[0, 0] == np.float32(1.0 + 2.0 ** -23)
-    # a short last block (H = 100: blocks of 64 and 36 columns)
-    x = _spike_row(100, [0, 64, 99], [1.0, 2.0 ** -12, 2.0 ** -12])
+    x = _spike_row(100, [3, 50, 99], [2.0 ** -12, 2.0 ** -12, 1.0])
     assert oracle.logits(x, x)[0, 0] == np.float32(1.0 + 2.0 ** -23)
 
 
