@@ -7,9 +7,9 @@
  *    shared expert ("Apple silicon용 Lily, Qwen 추론 최적화", aitrends.kr,
  *    section "Qwen 구조와 Prefill 경로"; "Perplexity Lily 오픈소스 공개",
  *    alltoptrend.co.kr, section 4).  The rule is: router logits
- *    l[t,e] = sum_h x[t,h]*Wr[e,h] (+ bias[e]) in fp32 in a fixed order
- *    (64-column blocks each summed in ascending h, the block sums added in
- *    block order), top_k by (logit descending, expert ascending), weights =
+ *    l[t,e] = sum_h x[t,h]*Wr[e,h] (+ bias[e]) in fp32, one sequential
+ *    chain in ascending h from zero with the bias added last, top_k by
+ *    (logit descending, expert ascending), weights =
  *    softmax of the chosen logits (norm_topk=1) or the full softmax
  *    probability (norm_topk=0).
  *  - Grouping without a host round trip: histogram of expert choices,
@@ -139,8 +139,8 @@ int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 
 /* Workspace bytes needed by moe_route (ws_kind = 0: expert histograms per
  * 64-token group, E * (ceil(T/64) rounded up to 4) int32, 256 fp32
- * router-row norms and the approximate router logits T * E fp32, each piece
- * 256-byte aligned) or moe_layer_forward (ws_kind = 1; also routing
+ * router-row norms, a piece-major copy of the router matrix E * H bf16 and
+ * the approximate router logits T * E fp32, each piece 256-byte aligned) or moe_layer_forward (ws_kind = 1; also routing
  * buffers, h and y).  Host-only, pure.  Workspace contents need no
  * initialization and are overwritten. */
 int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes);

@@ -55,7 +55,7 @@ Layout layout_of(const moe_layer_desc* d) {
     o = round_up(o + bytes, kAlign);
     return at;
   };
-  L.hist = take(route_workspace_bytes(d->T, d->E));
+  L.hist = take(route_workspace_bytes(d->T, d->H, d->E));
   L.ids = take(R * 4);
   L.w = take(R * 4);
   L.counts = take((size_t)d->E * 4);
@@ -180,7 +180,7 @@ int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!bytes || (ws_kind != 0 && ws_kind != 1)) return MOE_ERR_INVALID_ARGUMENT;
-  *bytes = ws_kind == 0 ? route_workspace_bytes(desc->T, desc->E) : layout_of(desc).total;
+  *bytes = ws_kind == 0 ? route_workspace_bytes(desc->T, desc->H, desc->E) : layout_of(desc).total;
   return MOE_OK;
 }
 
@@ -193,7 +193,7 @@ int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_r
   if ((rc = check_route_out(out))) return rc;
   if (misaligned(x) || misaligned(w_router) || misaligned(ws) || (router_bias && misaligned(router_bias)))
     return MOE_ERR_MISALIGNED;
-  if (ws_bytes < route_workspace_bytes(desc->T, desc->E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < route_workspace_bytes(desc->T, desc->H, desc->E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return do_route(desc, x, w_router, router_bias, out, ws, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -48,9 +48,9 @@ struct RouteArgs {
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
 };
-// Routing scratch (expert histograms per 64-token group, router-row norms,
-// approximate logits) and launcher.
-size_t route_workspace_bytes(int T, int E);
+// Routing scratch (expert histograms per 64-token group, router-row norms, a
+// piece-major copy of the router matrix, approximate logits) and launcher.
+size_t route_workspace_bytes(int T, int H, int E);
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream);
 
 struct GemmArgs {

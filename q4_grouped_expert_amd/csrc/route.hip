@@ -14,12 +14,11 @@ namespace moeq4 {
 // ---------------------------------------------------------------------------
 // Router logits and top-k.
 //
-// Logit contract: l[t,e] is an fp32 sum in a fixed order.  The hidden axis
-// splits into blocks of 64 columns; s_b = sum of x[t,h] * Wr[e,h] over block
-// b in ascending h, from 0; l = s_0 + s_1 + ... in block order, from 0; then
-// + bias[e].  A bf16 x bf16 product is exact in fp32, so an fma chain in that
-// order rounds exactly like "s = s + x*w"; every implementation that keeps
-// the order gets bit-identical logits and hence bit-identical expert ids.
+// Logit contract: l[t,e] is one fp32 chain over the hidden axis: acc = 0,
+// then acc = acc + x[t,h] * Wr[e,h] for h = 0, 1, ..., H-1, then + bias[e].
+// A bf16 x bf16 product is exact in fp32, so an fma chain in that order
+// rounds exactly like "acc = acc + x*w"; every implementation that keeps the
+// order gets bit-identical logits and hence bit-identical expert ids.
 //
 // Computing all T*E logits on the fp32 VALU costs 2*T*H*E flops.  Instead:
 //  1. approximate logits a[t,e] with bf16 MFMA (fp32 accumulation, any
@@ -28,8 +27,8 @@ namespace moeq4 {
 //     with sum_h |x w| <= ||x_t|| * max_e ||w_e|| =: S (Cauchy-Schwarz),
 //     da = 34 (H/32 + 1) 2^-23 S  (each 32-product MFMA step off by at most
 //     33 fp32 ulps of its inputs, for any summation order or truncation),
-//     dc = (H + 2) 2^-24 S  (bounds any order of fp32 summation of H terms,
-//     the blocked order included);
+//     dc = (H + 2) 2^-24 S  (bounds the rounding of an fp32 sum of H terms
+//     in any order, the bias add included);
 //  3. with tau = the K-th largest a[t,.], every expert outside
 //     {e : a[t,e] >= tau - 2 (da + dc)} has a canonical logit strictly below
 //     the K-th largest canonical logit, so it cannot be selected;
@@ -41,14 +40,18 @@ namespace moeq4 {
 // ---------------------------------------------------------------------------
 
 namespace {
-constexpr int kSelTokens = 4;    // tokens per selection workgroup (one wave each)
-constexpr int kLogitBlock = 64;  // columns per block of the canonical logit order
+constexpr int kSelTokens = 16;                    // tokens per selection workgroup
+constexpr int kXfStride = MOE_MAX_REDUCTION + 4;  // fp32 per token row in LDS (16-byte pad)
 }  // namespace
 
-// ||w_e||_2 of every router row, one wave per expert; the workgroups also
-// clear the expert histograms that the selection kernel accumulates into.
-__global__ __launch_bounds__(64) void route_wnorm_kernel(const uint16_t* __restrict__ wr, int H, float* wn,
-                                                         int32_t* __restrict__ hist, int hist_len) {
+// ||w_e||_2 of every router row, and the router matrix copied piece-major:
+// wt[p][e][0..7] = Wr[e][8p .. 8p+7] (p < H/8), so that piece p of
+// neighbouring experts shares a cache line.  One wave per expert; the
+// workgroups also clear the expert histograms that the selection kernel
+// accumulates into.
+__global__ __launch_bounds__(64) void route_wprep_kernel(const uint16_t* __restrict__ wr, int H, int E, float* wn,
+                                                         uint16_t* __restrict__ wt, int32_t* __restrict__ hist,
+                                                         int hist_len) {
   const int e = blockIdx.x, lane = threadIdx.x;
   for (int i = e * 64 + lane; i < hist_len; i += gridDim.x * 64) hist[i] = 0;
   // H <= 2048: at most four 16-byte pieces per lane, all loaded before use
@@ -60,13 +63,16 @@ __global__ __launch_bounds__(64) void route_wnorm_kernel(const uint16_t* __restr
   }
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i)
+  for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
+    const int h = 8 * lane + 512 * i;
+    if (h < H) *reinterpret_cast<u32x4*>(wt + ((size_t)(h / 8) * E + e) * 8) = v[i];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float lo = bf16_bits_to_f32(v[i][q] & 0xFFFFu), hi = bf16_bits_to_f32(v[i][q] >> 16);
       s = __builtin_fmaf(lo, lo, s);
       s = __builtin_fmaf(hi, hi, s);
     }
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) wn[e] = sqrtf(s);
@@ -270,97 +276,124 @@ __device__ __forceinline__ float chain8(float acc, float4 x0, float4 x1, u32x4 w
         [xc] "v"(x0.z), [xd] "v"(x0.w), [xe] "v"(x1.x), [xf] "v"(x1.y), [xg] "v"(x1.z), [xh] "v"(x1.w));
   return acc;
 }
+// m[j] = mask of the lanes whose k[j] >= c[j] (c wave-uniform), for four
+// tokens j.  The four compares sit in one block so that they issue back to
+// back and the scalar unit reads their masks after one wait, instead of one
+// vector-to-scalar wait per compare.  The outputs are early-clobber: a mask
+// written early must not land on a threshold register a later compare reads.
+__device__ __forceinline__ void ballot_ge4(uint64_t (&m)[4], const uint32_t (&k)[4], const uint32_t (&c)[4]) {
+  asm("v_cmp_le_u32_e64 %0, %4, %8\n\tv_cmp_le_u32_e64 %1, %5, %9\n\t"
+      "v_cmp_le_u32_e64 %2, %6, %10\n\tv_cmp_le_u32_e64 %3, %7, %11"
+      : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3])
+      : "s"(c[0]), "s"(c[1]), "s"(c[2]), "s"(c[3]), "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]));
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Selection: candidates from the approximate logits, canonical logits for the
 // candidates only, exact top-k, combine weights, expert histogram.
 //
-// One workgroup = 4 tokens; wave w owns token w in the per-token steps.  The
-// canonical logits of all the workgroup's candidates are spread as pairs of
-// chains over the waves: lane l of a pair computes block l % 32 of chain
-// l / 32 (one block sum, a 64-step fma chain), the block sums meet in LDS
-// and lane 0 of each half adds them in block order.  Token rows sit in LDS
-// as fp32 with each block's 16-byte chunks rotated by the block index, so
-// the 16 lanes of an LDS cycle read 16 different bank groups.
+// One workgroup = 16 tokens; in the per-token steps wave w owns tokens
+// 4w .. 4w+3.  The candidate chains (token, expert) of all 16 tokens are
+// listed in expert order and run one per lane, each a full sequential fp32
+// chain over the hidden axis: the token row comes from LDS as fp32 (rows
+// padded by 16 bytes so that 16 different rows hit 16 different bank
+// groups), the router row from the piece-major copy wt, where a wave's
+// experts, being sorted, share cache lines.  Router pieces stream P pieces
+// ahead of use in registers.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
                                                            const float* __restrict__ wn,
+                                                           const uint16_t* __restrict__ wt,
                                                            int32_t* __restrict__ hist, int ngp) {
   constexpr int TB = kSelTokens;
-  __shared__ __attribute__((aligned(16))) float xf[TB * MOE_MAX_REDUCTION];
-  // canonical logits of the candidates as keys: fkey(logit) << 8 | 255 - e
-  // (larger key = larger logit, then lower expert; E <= 256)
-  __shared__ unsigned long long ck[TB][MOE_MAX_EXPERTS];
-  __shared__ short cand[TB][MOE_MAX_EXPERTS];
-  // block sums of a wave's last (up to) 4 chain pairs, [pair % 4][lane]
-  __shared__ __attribute__((aligned(16))) float part[TB][4][64];
-  __shared__ float selv[TB][MOE_MAX_TOPK];
-  __shared__ int ccount[TB];
+  constexpr int TPW = TB / 4;                 // tokens per wave in the per-token steps
+  static_assert(TPW == 4, "the candidate search handles four tokens per wave");
+  constexpr int NP = MOE_MAX_REDUCTION / 512;  // 16-byte row pieces per lane
+  __shared__ __attribute__((aligned(16))) float xf[TB * kXfStride];
+  // candidates per token, in the order their chains finish: fkey of the
+  // canonical logit, and the expert
+  __shared__ uint32_t ckv[TB][MOE_MAX_EXPERTS];
+  __shared__ uint8_t cke[TB][MOE_MAX_EXPERTS];
+  __shared__ uint32_t emask[MOE_MAX_EXPERTS];  // bit tk: expert e is a candidate of token tk
+  __shared__ int estart[MOE_MAX_EXPERTS + 1];  // chains of the experts below e
+  __shared__ int wsum[4];
+  __shared__ int ccount[TB], cfill[TB];
+  __shared__ float lmax[TB];      // largest canonical logit per token
+  __shared__ float evs[TB][16];  // softmax terms by slot (tokens with at most 16 candidates)
   __shared__ float wmax_s, xn_s[TB];
   __shared__ int bhist[MOE_MAX_EXPERTS];
-  __shared__ float bias_s[MOE_MAX_EXPERTS];  // router bias (read in the chain loop without a global load)
+  __shared__ float bias_s[MOE_MAX_EXPERTS];  // router bias (read after the chains without a global load)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
   const int T = a.T, H = a.H, E = a.E, K = a.K;
-  const int nblk = H / kLogitBlock;
   const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
-  const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
-  // fp32 position of column h of token row r in LDS
-  auto xpos = [&](int r, int h) {
-    const int b = h >> 6, q = (h >> 2) & 15;
-    return r * MOE_MAX_REDUCTION + 64 * b + 4 * (q ^ (b & 15));
-  };
+  const rsrc_t w_rs = rsrc_of(wt, (uint32_t)E * H * 2u);
 
   bhist[tid] = 0;
-  bias_s[tid] = a.router_bias && tid < E ? a.router_bias[tid] : 0.0f;
-  const int t = t0 + wave;
-  const bool tvalid = t < T;
-  // approximate logits of token w, lane holding experts 4 lane .. 4 lane + 3
-  // (loaded now so their latency overlaps the token row's)
-  float av[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = 4 * lane + j;
-    av[j] = tvalid && e < E ? alog[(size_t)t * E + e] : 0.0f;
-  }
-  // ---- token row of wave w to fp32 in LDS, its norm; largest router-row norm
+  emask[tid] = 0u;
+  if (tid < TB) cfill[tid] = 0;
+  // router bias: loaded now, stored to LDS once the row loads are issued
+  const float rb = a.router_bias && tid < E ? a.router_bias[tid] : 0.0f;
+
+  // ---- token rows of wave w to fp32 in LDS, their norms; approximate logits
+  // of its tokens (lane holding experts 4 lane .. 4 lane + 3); all loads of
+  // the step are issued before any is used
+  float av[TPW][4];
   {
-    const bool tv = tvalid;
-    u32x4 v[MOE_MAX_REDUCTION / 512];
+    u32x4 v[TPW][NP];
 #pragma unroll
-    for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
-      const int h = 8 * lane + 512 * i;
-      const uint32_t off = tv && h < H ? ((uint32_t)t * H + h) * 2u : kOob;
-      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t0 + TPW * wave + j;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int h = 8 * lane + 512 * i;
+        const uint32_t off = t < T && h < H ? ((uint32_t)t * H + h) * 2u : kOob;
+        v[j][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t0 + TPW * wave + j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * lane + q;
+        av[j][q] = t < T && e < E ? alog[(size_t)t * E + e] : 0.0f;
+      }
     }
     float wv[MOE_MAX_EXPERTS / 64];
     if (wave == 0) {
 #pragma unroll
       for (int i = 0; i < MOE_MAX_EXPERTS / 64; ++i) wv[i] = lane + 64 * i < E ? wn[lane + 64 * i] : 0.0f;
     }
-    float s2 = 0.0f;
+    bias_s[tid] = rb;
 #pragma unroll
-    for (int i = 0; i < MOE_MAX_REDUCTION / 512; ++i) {
-      const int h = 8 * lane + 512 * i;
-      if (h < H) {
-        float f[8];
+    for (int j = 0; j < TPW; ++j) {
+      const int tk = TPW * wave + j;
+      float s2 = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f[2 * q] = bf16_bits_to_f32(v[i][q] & 0xFFFFu);
-          f[2 * q + 1] = bf16_bits_to_f32(v[i][q] >> 16);
+      for (int i = 0; i < NP; ++i) {
+        const int h = 8 * lane + 512 * i;
+        if (h < H) {
+          float f[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f[2 * q] = bf16_bits_to_f32(v[j][i][q] & 0xFFFFu);
+            f[2 * q + 1] = bf16_bits_to_f32(v[j][i][q] >> 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) s2 = __builtin_fmaf(f[q], f[q], s2);
+          float4* dst = reinterpret_cast<float4*>(&xf[tk * kXfStride + h]);
+          dst[0] = float4{f[0], f[1], f[2], f[3]};
+          dst[1] = float4{f[4], f[5], f[6], f[7]};
         }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s2 = __builtin_fmaf(f[q], f[q], s2);
-        *reinterpret_cast<float4*>(&xf[xpos(wave, h)]) = float4{f[0], f[1], f[2], f[3]};
-        *reinterpret_cast<float4*>(&xf[xpos(wave, h + 4)]) = float4{f[4], f[5], f[6], f[7]};
       }
-    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
-    if (lane == 0) xn_s[wave] = sqrtf(s2);
+      for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+      if (lane == 0) xn_s[tk] = sqrtf(s2);
+    }
     if (wave == 0) {
       float m = 0.0f;
 #pragma unroll
@@ -372,202 +405,243 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   }
   __syncthreads();
 
-  // ---- candidates of token w ---------------------------------------------
+  // ---- candidates of the wave's tokens -----------------------------------
+  // tau_j <= the K-th largest approximate logit of token j.  Each lane takes
+  // the largest of its four keys; the K-th largest of these lane maxima is at
+  // most the K-th largest key (the K largest lane maxima are K different
+  // keys).  th = the largest 16-bit key prefix with at least K lane maxima at
+  // or above it, built bit by bit (wave-uniform, the wave's tokens side by
+  // side), so th << 16 is at most the K-th largest key; a lower tau only
+  // widens the candidate set.  With fewer than K lanes holding keys
+  // (E < 4K) no prefix qualifies and every expert is a candidate.
   {
-    const float* v = av;
-    uint32_t key[4];
+    uint32_t mk[TPW], th[TPW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = tvalid && 4 * lane + j < E ? fkey(v[j]) >> 16 : 0u;
-    // tau <= the K-th largest approximate logit: th = the largest 16-bit key
-    // prefix with at least K keys at or above it, built bit by bit
-    // (wave-uniform); th << 16 is at most the K-th largest key, and a lower
-    // tau only widens the candidate set
-    uint32_t th = 0;
+    for (int j = 0; j < TPW; ++j) {
+      const bool tvalid = t0 + TPW * wave + j < T;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m = max(m, tvalid && 4 * lane + q < E ? fkey(av[j][q]) >> 16 : 0u);
+      mk[j] = m;
+      th[j] = 0u;
+    }
+#pragma unroll
     for (int bit = 15; bit >= 0; --bit) {
-      const uint32_t c = th | (1u << bit);
-      int n = 0;
+      uint32_t c[TPW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) n += __popcll(__ballot(key[j] >= c));
-      if (n >= K) th = c;
-    }
-    const float tau = fkey_inv(th << 16);
-    float win;
-    if (!a.norm_topk) {
-      win = INFINITY;
-    } else {
-      const float S = xn_s[wave] * wmax_s * 1.001f;
-      const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
-      const float dc = (float)(H + 2) * 0x1p-24f * S;
-      win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
-    }
-    // compact the candidates in expert order
-    bool f[4];
-    uint64_t bal[4];
-    int below = 0, total = 0;
+      for (int j = 0; j < TPW; ++j) c[j] = th[j] | (1u << bit);
+      uint64_t m[TPW];
+      ballot_ge4(m, mk, c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[j] = tvalid && 4 * lane + j < E && v[j] >= tau - win;
-      bal[j] = __ballot(f[j]);
-      below += __popcll(bal[j] & lanes_below());
-      total += __popcll(bal[j]);
+      for (int j = 0; j < TPW; ++j)
+        if (__popcll(m[j]) >= K) th[j] = c[j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (f[j]) cand[wave][below++] = (short)(4 * lane + j);
-    if (lane == 0) ccount[wave] = total;
+    for (int j = 0; j < TPW; ++j) {
+      const int tk = TPW * wave + j;
+      const bool tvalid = t0 + tk < T;
+      const float tau = th[j] ? fkey_inv(th[j] << 16) : -INFINITY;
+      float win;
+      if (!a.norm_topk) {
+        win = INFINITY;
+      } else {
+        const float S = xn_s[tk] * wmax_s * 1.001f;
+        const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
+        const float dc = (float)(H + 2) * 0x1p-24f * S;
+        win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
+      }
+      int total = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool f = tvalid && 4 * lane + q < E && av[j][q] >= tau - win;
+        total += __popcll(__ballot(f));
+        if (f) atomicOr(&emask[4 * lane + q], 1u << tk);
+      }
+      if (lane == 0) ccount[tk] = total;
+    }
   }
   __syncthreads();
 
-  // ---- canonical logits of all candidates, two chains per wave pass ------
+  // ---- chain list in expert order: exclusive scan of the candidate counts
   {
-    int cst[TB + 1];
-    cst[0] = 0;
+    const int n = __popc(emask[tid]);
+    int inc = n;
 #pragma unroll
-    for (int i = 0; i < TB; ++i) cst[i + 1] = cst[i] + ccount[i];
-    const int nchain = cst[TB];
-    const int npair = (nchain + 1) / 2;
-    const int half = lane >> 5, b = lane & 31;
-    // chain c -> (token slot, expert); row offset of this lane's block, or
-    // an offset that reads zeros
-    auto locate = [&](int c, int& tk, int& slot, int& e) {
-      tk = 0;
-#pragma unroll
-      for (int i = 1; i < TB; ++i) tk += c >= cst[i] ? 1 : 0;
-      slot = c - cst[tk];
-      e = cand[tk][slot];
-    };
-    auto row_off = [&](int p) -> uint32_t {
-      const int c = 2 * p + half;
-      if (p >= npair || c >= nchain || b >= nblk) return kOob;
-      int tk, slot, e;
-      locate(c, tk, slot, e);
-      return ((uint32_t)e * H + kLogitBlock * b) * 2u;
-    };
-    auto load = [&](u32x4 (&w)[8], uint32_t off) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, off, 16 * i, 0));
-    };
-    // block sum of pair p from this lane's router block w
-    auto block_sum = [&](const u32x4 (&w)[8], int p) -> float {
-      const int c = 2 * p + half;
-      int tk = 0;
-#pragma unroll
-      for (int i = 1; i < TB; ++i) tk += c >= cst[i] ? 1 : 0;
-      float sb = 0.0f;
-      const float* xr = &xf[tk * MOE_MAX_REDUCTION + kLogitBlock * b];
-      const int sw = b & 15;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&xr[4 * ((2 * i) ^ sw)]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&xr[4 * ((2 * i + 1) ^ sw)]);
-        sb = chain8(sb, x0, x1, w[i]);
-      }
-      return sb;
-    };
-    // Block sums go to LDS, one row of 64 per pair; after every 4th pair of
-    // the wave (and after its last) lane j < 8 adds the block sums of chain
-    // j of those pairs in block order, so the 32-add chains of 8 chains run
-    // side by side.  p0 is the wave's first pair of the batch, n its size.
-    auto combine = [&](int p0, int n) {
-      __builtin_amdgcn_wave_barrier();
-      const int j = lane;          // chain 2 (p0 + TB (j / 2)) + j % 2
-      const int pj = p0 + TB * (j >> 1);
-      const int c = 2 * pj + (j & 1);
-      if (j < 2 * n && c < nchain) {
-        int tk, slot, e;
-        locate(c, tk, slot, e);
-        const float* row = &part[wave][j >> 1][32 * (j & 1)];
-        float ps[32];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 q = *reinterpret_cast<const float4*>(&row[4 * i]);
-          ps[4 * i] = q.x;
-          ps[4 * i + 1] = q.y;
-          ps[4 * i + 2] = q.z;
-          ps[4 * i + 3] = q.w;
-        }
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (i < nblk) acc = acc + ps[i];
-        if (a.router_bias) acc = acc + bias_s[e];
-        ck[tk][slot] = ((unsigned long long)fkey(acc) << 8) | (unsigned)(255 - e);
-      }
-      __builtin_amdgcn_wave_barrier();
-    };
-    u32x4 wa[8], wb[8];
-    uint32_t offa = row_off(wave);
-    load(wa, offa);
-    int it = 0;  // pairs of this wave so far
-    for (int p = wave; p < npair; p += 2 * TB) {
-      uint32_t offb = row_off(p + TB);
-      load(wb, offb);
-      const float sa = block_sum(wa, p);
-      // the reload of wa must follow its last use (else a second register
-      // set and a full wait at the back edge): tie its offset to sa
-      offa = row_off(p + 2 * TB);
-      asm("" : "+v"(offa) : "v"(sa));
-      load(wa, offa);
-      part[wave][it & 3][lane] = sa;
-      ++it;
-      if (p + TB < npair) {
-        part[wave][it & 3][lane] = block_sum(wb, p + TB);
-        ++it;
-      }
-      if ((it & 3) == 0) combine(wave + TB * (it - 4), 4);
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o);
+      if (lane >= o) inc += u;
     }
-    if (it & 3) combine(wave + TB * (it & ~3), it & 3);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    estart[tid] = base + inc - n;
+    if (tid == MOE_MAX_EXPERTS - 1) estart[MOE_MAX_EXPERTS] = base + inc;
   }
   __syncthreads();
 
-  // ---- exact top-k of token w among its candidates -----------------------
-  // A candidate's slot is the number of its token's candidates with a larger
-  // key (keys are distinct); the K smallest slots are the selection, already
-  // in slot order.
-  if (tvalid) {
-    const int C = ccount[wave];
-    const unsigned long long* kw = ck[wave];
-    unsigned long long mine[MOE_MAX_EXPERTS / 64];
-    int rank[MOE_MAX_EXPERTS / 64];
+  // ---- canonical logits: acc = 0, acc += x[t,h] * Wr[e,h] for h ascending,
+  // then + bias; bf16 x bf16 products are exact in fp32, so each fma rounds
+  // exactly like "acc = acc + x*w".  Chain c runs on thread c % 256 of pass
+  // c / 256; piece p (columns 8p .. 8p+7) of expert e sits at wt + (p E + e) 8.
+  const int npc = H / 8;
+  auto chains = [&](auto depth) {
+    constexpr int P = decltype(depth)::value;
+    const int nch = estart[MOE_MAX_EXPERTS];
+    for (int c0 = 0; c0 < nch; c0 += 256) {
+      const int c = c0 + tid;
+      const bool live = c < nch;
+      // expert: the last e with estart[e] <= c; token: the (c - estart[e])-th
+      // set bit of emask[e]
+      int lo = 0, hi = MOE_MAX_EXPERTS;
 #pragma unroll
-    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
-      const int c = lane + 64 * r;
-      mine[r] = c < C ? kw[c] : 0ull;
-      rank[r] = C;
-      if (64 * r < C) {
-        int n = 0;
-#pragma unroll 4
-        for (int o = 0; o < C; ++o) n += kw[o] > mine[r] ? 1 : 0;
-        rank[r] = n;
-        if (c < C && n < K) selv[wave][n] = fkey_inv((uint32_t)(mine[r] >> 8));
+      for (int s = 0; s < 8; ++s) {
+        const int mid = (lo + hi) >> 1;
+        if (estart[mid] <= c) lo = mid;
+        else hi = mid;
+      }
+      const int e = lo;
+      uint32_t m = live ? emask[e] : 1u;
+      for (int r = live ? c - estart[e] : 0; r > 0; --r) m &= m - 1u;
+      const int tk = __builtin_ctz(m);
+      const uint32_t voff = live ? (uint32_t)e * 16u : kOob;
+      const float* xr = &xf[tk * kXfStride];
+      const uint32_t pstride = (uint32_t)E * 16u;  // bytes from one piece to the next
+      // first group in piece order (the loop's waits assume wb[i] was issued
+      // i-th, on entry as on the back edge)
+      u32x4 wb[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        wb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, voff, i * pstride, 0));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float acc = 0.0f;
+      uint32_t vo = voff;
+      for (int p0 = 0; p0 < npc; p0 += P) {
+        const int nxt = p0 + P < npc ? p0 + P : p0;  // the last group re-reads itself
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i)]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&xr[8 * (p0 + i) + 4]);
+          acc = chain8(acc, x0, x1, wb[i]);
+          // Reload wb[i] only after its last use: the empty asm makes the
+          // offset depend on acc, so the scheduler cannot hoist the load (a
+          // hoisted load needs a second register set, copied back behind a
+          // full wait at the loop's back edge).
+          asm("" : "+v"(vo) : "v"(acc));
+          wb[i] = __builtin_bit_cast(u32x4,
+                                     __builtin_amdgcn_raw_buffer_load_b128(w_rs, vo, (nxt + i) * pstride, 0));
+        }
+      }
+      if (live) {
+        if (a.router_bias) acc = acc + bias_s[e];
+        const int slot = atomicAdd(&cfill[tk], 1);
+        ckv[tk][slot] = fkey(acc);
+        cke[tk][slot] = (uint8_t)e;
       }
     }
+  };
+  if (npc % 16 == 0)
+    chains(std::integral_constant<int, 16>{});
+  else
+    chains(std::integral_constant<int, 8>{});
+  __syncthreads();
+
+  // ---- exact top-k of each token among its candidates --------------------
+  // A candidate's slot is the number of its token's candidates with a larger
+  // key (logit, then lower expert; keys are distinct); the K smallest slots
+  // are the selection, already in slot order.  Combine weights: exp(l - max)
+  // over the sum of exp(l - max) of the selection (norm_topk) or of every
+  // expert, the sums taken across lanes.
+  auto ckey = [&](int tk, int c) -> unsigned long long {
+    return ((unsigned long long)ckv[tk][c] << 8) | (unsigned)(255 - cke[tk][c]);
+  };
+  auto emit = [&](int t, int rank, int e, float w) {
+    a.out.topk_ids[(size_t)t * K + rank] = e;
+    a.out.topk_w[(size_t)t * K + rank] = w;
+    atomicAdd(&bhist[e], 1);
+  };
+  bool small = true;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) small = small && ccount[TPW * wave + j] <= 16;
+  if (small) {
+    // the wave's tokens side by side, 16 lanes each, one candidate per lane
+    const int j = lane >> 4, sl = lane & 15;
+    const int tk = TPW * wave + j;
+    const int C = ccount[tk];  // 0 for tokens past T
+    const bool valid = sl < C;
+    const unsigned long long my = valid ? ckey(tk, sl) : 0ull;
+    int n = 0;
+#pragma unroll
+    for (int o = 0; o < 16; ++o) n += o < C && ckey(tk, o) > my ? 1 : 0;
+    const float v = fkey_inv((uint32_t)(my >> 8));
+    if (valid && n == 0) lmax[tk] = v;
     __builtin_amdgcn_wave_barrier();
-    const float mx = selv[wave][0];
-    float den = 0.0f;
-    if (a.norm_topk) {
-      for (int k = 0; k < K; ++k) den += expf(selv[wave][k] - mx);
-    } else {
-      float sum = 0.0f;
+    const float ev = valid ? expf(v - lmax[tk]) : 0.0f;
+    // the sum runs over the terms placed by slot, in a fixed tree, so the
+    // weights do not depend on the order the chains finished in
+    if (valid) evs[tk][n] = ev;
+    __builtin_amdgcn_wave_barrier();
+    float part = sl < C && (!a.norm_topk || sl < K) ? evs[tk][sl] : 0.0f;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) part += __shfl_xor(part, o, 16);
+    if (valid && n < K) emit(t0 + tk, n, 255 - (int)(my & 255ull), ev / part);
+  } else {
+#pragma unroll 1
+    for (int j = 0; j < TPW; ++j) {
+      const int tk = TPW * wave + j;
+      const int C = ccount[tk];
+      float v[MOE_MAX_EXPERTS / 64];
+      int me[MOE_MAX_EXPERTS / 64], rank[MOE_MAX_EXPERTS / 64];
+#pragma unroll
+      for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
+        const int c = lane + 64 * r;
+        rank[r] = K;
+        me[r] = 0;
+        v[r] = 0.0f;
+        if (64 * r < C) {
+          const unsigned long long my = c < C ? ckey(tk, c) : 0ull;
+          int n = 0;
+#pragma unroll 4
+          for (int o = 0; o < C; ++o) n += ckey(tk, o) > my ? 1 : 0;
+          me[r] = 255 - (int)(my & 255ull);
+          v[r] = fkey_inv((uint32_t)(my >> 8));
+          if (c < C) {
+            rank[r] = n;
+            if (n == 0) lmax[tk] = v[r];
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float mx = C > 0 ? lmax[tk] : 0.0f;
+      // terms placed by slot (over the keys, which every lane has read; same
+      // element type, so the stores stay behind those reads), then summed in
+      // a fixed tree: lane l adds slots 4l .. 4l+3
+      float ev[MOE_MAX_EXPERTS / 64];
+#pragma unroll
+      for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
+        ev[r] = 0.0f;
+        if (lane + 64 * r < C) {
+          ev[r] = expf(v[r] - mx);
+          ckv[tk][rank[r]] = __float_as_uint(ev[r]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int nterm = a.norm_topk ? K : C;
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lane + i < nterm) part += __uint_as_float(ckv[tk][4 * lane + i]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
 #pragma unroll
       for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r)
-        if (lane + 64 * r < C) sum += expf(fkey_inv((uint32_t)(mine[r] >> 8)) - mx);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-      den = sum;
-    }
-#pragma unroll
-    for (int r = 0; r < MOE_MAX_EXPERTS / 64; ++r) {
-      if (lane + 64 * r < C && rank[r] < K) {
-        const int e = 255 - (int)(mine[r] & 255ull);
-        a.out.topk_ids[(size_t)t * K + rank[r]] = e;
-        a.out.topk_w[(size_t)t * K + rank[r]] = expf(selv[wave][rank[r]] - mx) / den;
-        atomicAdd(&bhist[e], 1);
-      }
+        if (rank[r] < K) emit(t0 + tk, rank[r], me[r], ev[r] / part);
     }
   }
-  __syncthreads();
+  // LDS-only barrier: the histogram atomics above must land, the global
+  // stores need not
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // this workgroup's tokens lie in one histogram group of kHistTokens;
   // hist is [E][ngp]
   if (tid < E && bhist[tid]) atomicAdd(&hist[(size_t)tid * ngp + t0 / kHistTokens], bhist[tid]);
@@ -701,38 +775,41 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
 namespace {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct RouteWs {
-  size_t hist, wn, alog, total;
+  size_t hist, wn, wt, alog, total;
 };
 // expert-histogram row length: 64-token groups rounded up to 4
 int hist_row(int T) { return ((T + kHistTokens - 1) / kHistTokens + 3) & ~3; }
-RouteWs route_ws_layout(int T, int E) {
+RouteWs route_ws_layout(int T, int H, int E) {
   const size_t ng = (size_t)hist_row(T);
   RouteWs L;
   L.hist = 0;                                                     // expert histograms [E][64-token groups]
   L.wn = align256(ng * (size_t)E * sizeof(int32_t));             // router row norms
-  L.alog = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));      // approximate logits [T][E]
+  L.wt = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));        // piece-major router copy [H/8][E][8] bf16
+  L.alog = L.wt + align256((size_t)E * H * sizeof(uint16_t));     // approximate logits [T][E]
   L.total = L.alog + align256((size_t)T * E * sizeof(float));
   return L;
 }
 }  // namespace
 
-size_t route_workspace_bytes(int T, int E) { return route_ws_layout(T, E).total; }
+size_t route_workspace_bytes(int T, int H, int E) { return route_ws_layout(T, H, E).total; }
 
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   const int ng = (a.T + kHistTokens - 1) / kHistTokens, ngp = hist_row(a.T);
-  const RouteWs L = route_ws_layout(a.T, a.E);
+  const RouteWs L = route_ws_layout(a.T, a.H, a.E);
   char* base = reinterpret_cast<char*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   float* wn = reinterpret_cast<float*>(base + L.wn);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(base + L.wt);
   float* alog = reinterpret_cast<float*>(base + L.alog);
-  hipLaunchKernelGGL(route_wnorm_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, wn, hist, ngp * a.E);
+  hipLaunchKernelGGL(route_wprep_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, a.E, wn, wt, hist,
+                     ngp * a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
   hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb), dim3(256), 0, stream, a, ntb, neb, alog);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_select_kernel, dim3((a.T + kSelTokens - 1) / kSelTokens), dim3(256), 0, stream, a, alog,
-                     wn, hist, ngp);
+                     wn, wt, hist, ngp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_group_kernel, dim3(ng), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ngp, a.T, a.K, a.E,
                      a.has_shared, a.out);

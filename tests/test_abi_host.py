@@ -140,7 +140,7 @@ def test_entry_point_argument_errors():
                        1 << 20, None) == B.MOE_ERR_MISALIGNED
     need = B.moe_workspace_size(d, 0)
     a256 = lambda n: (n + 255) // 256 * 256
-    assert need == a256(4 * 16 * 4) + 256 * 4 + a256(64 * 16 * 4)
+    assert need == a256(4 * 16 * 4) + 256 * 4 + a256(16 * 256 * 2) + a256(64 * 16 * 4)
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), A, need - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -159,6 +159,7 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     assert big >= rows * 512 * 2 + rows * 2048 * 4
     assert big > small
     # routing scratch: expert histograms [E][64-token groups rounded up to 4]
-    # int32, 256 router-row norms and approximate logits [T][E] fp32
+    # int32, 256 router-row norms, the piece-major router copy [H/8][E][8]
+    # bf16 and approximate logits [T][E] fp32
     assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == (
-        64 * 256 * 4 + 256 * 4 + 4096 * 256 * 4)
+        64 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 4096 * 256 * 4)
