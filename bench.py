@@ -76,6 +76,10 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill4096",
                     help="prefill4096 (default), prefill512, skew2048, long16384 or tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--variant", default="fused", choices=["fused", "unfused_dequant", "host_sync"],
+                    help="fused: the layer as built (default); unfused_dequant: a separate kernel writes the bf16 "
+                         "weights of the experts with rows, then a bf16 grouped GEMM reads them; host_sync: the "
+                         "host reads the tile count after routing and sizes the GEMM launches from it")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle is timed on (from the first)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -121,26 +125,66 @@ def main() -> int:
     sgu = dl.s_gate_up.desc if dl.has_shared else None
     sdn = dl.s_down.desc if dl.has_shared else None
 
+    variant = args.variant
+    if variant == "unfused_dequant":
+        # bf16 weight buffers the separate dequant kernel writes (experts with rows)
+        i16 = dict(dtype=torch.int16, device=dev)
+        wgu, wdn = torch.empty((E, 2 * I, H), **i16), torch.empty((E, H, I), **i16)
+        bgu, bdn = B.bf16_desc(wgu, E, 2 * I, H), B.bf16_desc(wdn, E, H, I)
+        bgu_s = bdn_s = None
+        if dl.has_shared:
+            wgu_s, wdn_s = torch.empty((1, 2 * I, H), **i16), torch.empty((1, H, I), **i16)
+            bgu_s, bdn_s = B.bf16_desc(wgu_s, 1, 2 * I, H), B.bf16_desc(wdn_s, 1, H, I)
+
+        def dequant(w, w_bf, s_w, s_bf):
+            B.moe_dequant_q4_to_bf16(w, route["counts"], w_bf, stream)
+            if s_w is not None:
+                B.moe_dequant_q4_to_bf16(s_w, None, s_bf, stream)
+
+    # phase names of one chunk, timed with events between them
+    names = {"fused": ["route", "gemm_gate_up", "gemm_down", "combine"],
+             "unfused_dequant": ["route", "dequant_gate_up", "gemm_gate_up", "dequant_down", "gemm_down",
+                                 "combine"],
+             "host_sync": ["layer"]}[variant]
+
     def step(events=None):
         for ci, (c0, c1) in enumerate(chunks):
             d = dl.desc(c1 - c0)
             ev = events[ci] if events is not None else None
-            if ev: ev[0].record(stream)
+            mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+            mark(0)
+            if variant == "host_sync":
+                B.moe_layer_forward_host_sync(d, dl.x[c0:c1], dl.w_router, dl.router_bias, dl.gate_up.desc,
+                                              dl.down.desc, sgu, sdn, out[c0:c1], rdesc, dl.ws, dl.ws_bytes, stream)
+                mark(1)
+                continue
             B.moe_route(d, dl.x[c0:c1], dl.w_router, dl.router_bias, rdesc, dl.route_ws, dl.route_ws_bytes, stream)
-            if ev: ev[1].record(stream)
-            B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], dl.gate_up.desc, sgu, rdesc, h, stream)
-            if ev: ev[2].record(stream)
-            B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h, dl.down.desc, sdn, rdesc, y, stream)
-            if ev: ev[3].record(stream)
+            mark(1)
+            if variant == "fused":
+                B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], dl.gate_up.desc, sgu, rdesc, h,
+                                      stream)
+                mark(2)
+                B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h, dl.down.desc, sdn, rdesc, y, stream)
+                mark(3)
+            else:
+                dequant(dl.gate_up.desc, wgu, sgu, wgu_s if dl.has_shared else None)
+                mark(2)
+                B.moe_grouped_gemm_bf16(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], bgu, bgu_s, rdesc, h, stream)
+                mark(3)
+                dequant(dl.down.desc, wdn, sdn, wdn_s if dl.has_shared else None)
+                mark(4)
+                B.moe_grouped_gemm_bf16(d, B.MOE_GEMM_DOWN, h, bdn, bdn_s, rdesc, y, stream)
+                mark(5)
             B.moe_combine(d, y, rdesc, out[c0:c1], stream)
-            if ev: ev[4].record(stream)
+            mark(len(names))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item(), "non-finite layer output"
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in chunks] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in chunks]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -148,13 +192,14 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    names = ["route", "gemm_gate_up", "gemm_down", "combine"]
     per = {n: [] for n in names}
     for s in range(args.steps):
         for ev in evs[s]:
             for i, n in enumerate(names):
                 per[n].append(ev[i].elapsed_time(ev[i + 1]))
     kernels_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    if variant != "fused":
+        return report_variant(args, shape, dl, chunk, T, elapsed, kernels_ms)
 
     # algorithmic work of the dominant kernel (gate/up GEMM) per launch
     counts_last = route["counts"].cpu().numpy()
@@ -243,6 +288,34 @@ def main() -> int:
         res["cpu_baseline"] = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                                "sample": f"first {S} of the {T} tokens, whole layer (routing, dequant of every "
                                          f"expert with rows, SwiGLU FFN, combine), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def report_variant(args, shape, dl, chunk, T, elapsed, kernels_ms):
+    """One JSON line for an ablation variant: layer tokens/s and the per-phase
+    means of the variant (no roofline entry: that is the fused layer's)."""
+    ms_per_step = elapsed * 1e3 / args.steps
+    res = {
+        "metric": METRIC,
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: T={T} H={shape.H} I={shape.I} E={shape.E} top-{shape.K}"
+                        f"{' + 1 shared' if dl.has_shared else ''}, chunk={chunk}",
+            "variant": args.variant, "tokens": T, "chunk": chunk, "seed": shape.seed, "norm_topk": 1,
+        },
+        "phases_ms": {n: round(v, 4) for n, v in kernels_ms.items()},
+    }
     print(json.dumps(res), flush=True)
     return 0
 

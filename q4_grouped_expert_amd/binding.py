@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h).
+"""Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h and
+include/moe_q4_ablation.h).
 
 Argument marshalling only: torch tensors supply device memory and the HIP
 stream, every step of the layer runs in the library's HIP kernels.  There is
@@ -36,6 +37,10 @@ class Q4Desc(ctypes.Structure):
                 ("n_exp", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
 
 
+class Bf16Desc(ctypes.Structure):
+    _fields_ = [("w", c_p), ("n_exp", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+
+
 class LayerDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("has_shared", ctypes.c_int32)]
@@ -59,6 +64,14 @@ SIGNATURES = {
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
                                          ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                          c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
+    # the unfused-dequant and host-round-trip variants (moe_q4_ablation.h)
+    "moe_dequant_q4_to_bf16": (ctypes.c_int, [ctypes.POINTER(Q4Desc), c_p, c_p, c_p]),
+    "moe_grouped_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, c_p, ctypes.POINTER(Bf16Desc),
+                                             ctypes.POINTER(Bf16Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p]),
+    "moe_layer_forward_host_sync": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
+                                                   ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
+                                                   ctypes.POINTER(Q4Desc), c_p, ctypes.POINTER(RouteOutDesc), c_p,
+                                                   ctypes.c_size_t, c_p]),
 }
 
 _lib = None
@@ -168,3 +181,29 @@ def moe_layer_forward(desc, x, w_router, router_bias, w_gate_up: Q4Desc, w_down:
         ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), byref(w_gate_up), byref(w_down),
         byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes,
         _stream(stream)))
+
+
+def moe_layer_forward_host_sync(desc, x, w_router, router_bias, w_gate_up: Q4Desc, w_down: Q4Desc,
+                                shared_gate_up: Optional[Q4Desc], shared_down: Optional[Q4Desc], out,
+                                route: Optional[RouteOutDesc], ws, ws_bytes, stream=None):
+    byref = lambda d: ctypes.byref(d) if d is not None else None  # noqa: E731
+    _chk("moe_layer_forward_host_sync", lib().moe_layer_forward_host_sync(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), byref(w_gate_up), byref(w_down),
+        byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def bf16_desc(w, n_exp, N, K) -> Bf16Desc:
+    return Bf16Desc(_ptr(w), n_exp, N, K)
+
+
+def moe_dequant_q4_to_bf16(w: Q4Desc, counts, out, stream=None):
+    _chk("moe_dequant_q4_to_bf16", lib().moe_dequant_q4_to_bf16(ctypes.byref(w), _ptr(counts), _ptr(out),
+                                                                _stream(stream)))
+
+
+def moe_grouped_gemm_bf16(desc, mode, a, w: Bf16Desc, w_shared: Optional[Bf16Desc], route: RouteOutDesc, c,
+                          stream=None):
+    _chk("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
+        ctypes.byref(desc), mode, _ptr(a), ctypes.byref(w),
+        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _stream(stream)))

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "moe_q4_ablation.h"
 
 using namespace moeq4;
 
@@ -106,16 +107,29 @@ int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, con
   return hip_status(launch_route(a, ws, s));
 }
 
-int do_gemm(const moe_layer_desc* d, int mode, const void* a, const moe_q4_tensor* w, const moe_q4_tensor* ws,
-            const moe_route_out* r, void* c, hipStream_t s) {
+// Weights of one grouped GEMM: 4-bit (q, qs) or, for the unfused variant,
+// bf16 in memory (bf, bfs).  The shared expert's are null without one.
+struct GemmWeights {
+  const moe_q4_tensor* q = nullptr;
+  const moe_q4_tensor* qs = nullptr;
+  const uint16_t* bf = nullptr;
+  const uint16_t* bfs = nullptr;
+};
+
+// tiles > 0: launch exactly that many tiles (known on the host) instead of
+// the bound max_tiles_of(d).
+int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights& w, const moe_route_out* r, void* c,
+            hipStream_t s, int tiles = 0) {
   GemmArgs g;
   g.a = reinterpret_cast<const uint16_t*>(a);
-  g.codes = w->codes;
-  g.scales = w->scales;
-  g.biases = w->biases;
-  g.s_codes = ws ? ws->codes : nullptr;
-  g.s_scales = ws ? ws->scales : nullptr;
-  g.s_biases = ws ? ws->biases : nullptr;
+  g.codes = w.q ? w.q->codes : nullptr;
+  g.scales = w.q ? w.q->scales : nullptr;
+  g.biases = w.q ? w.q->biases : nullptr;
+  g.s_codes = w.qs ? w.qs->codes : nullptr;
+  g.s_scales = w.qs ? w.qs->scales : nullptr;
+  g.s_biases = w.qs ? w.qs->biases : nullptr;
+  g.wbf = w.bf;
+  g.s_wbf = w.bfs;
   g.sorted_idx = r->sorted_idx;
   g.block_map = r->block_map;
   g.n_tiles = r->n_tiles;
@@ -125,7 +139,7 @@ int do_gemm(const moe_layer_desc* d, int mode, const void* a, const moe_q4_tenso
   g.topk = d->top_k;
   g.R = d->T * d->top_k;
   g.I = d->I;
-  g.max_tiles = (int)max_tiles_of(d);
+  g.max_tiles = tiles > 0 ? tiles : (int)max_tiles_of(d);
   if (mode == MOE_GEMM_GATE_UP_SWIGLU) {
     g.N = 2 * d->I;
     g.Kdim = d->H;
@@ -148,6 +162,76 @@ int do_combine(const moe_layer_desc* d, const float* y, const moe_route_out* r, 
   c.R = d->T * d->top_k;
   c.has_shared = d->has_shared;
   return hip_status(launch_combine(c, s));
+}
+
+int check_bf16(const moe_bf16_tensor* t, int n_exp, int N, int K) {
+  if (!t || !t->w) return MOE_ERR_INVALID_ARGUMENT;
+  if (t->n_exp != n_exp || t->N != N || t->K != K) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (misaligned(t->w)) return MOE_ERR_MISALIGNED;
+  // one expert's bf16 matrix is addressed through 32-bit buffer offsets
+  if ((int64_t)N * K * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+// The layer for one chunk.  host_sync: after routing, copy n_tiles to the
+// host, wait for the stream and size the GEMM grids from it.
+int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                  const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
+                  const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null, void* ws,
+                  size_t ws_bytes, void* stream, bool host_sync) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->T == 0) return MOE_OK;
+  if (!x || !w_router || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if ((rc = check_q4(w_gate_up, desc->E, 2 * desc->I, desc->H))) return rc;
+  if ((rc = check_q4(w_down, desc->E, desc->H, desc->I))) return rc;
+  if (desc->has_shared) {
+    if ((rc = check_q4(shared_gate_up, 1, 2 * desc->I, desc->H))) return rc;
+    if ((rc = check_q4(shared_down, 1, desc->H, desc->I))) return rc;
+  } else {
+    shared_gate_up = shared_down = nullptr;
+  }
+  if (route_or_null && (rc = check_route_out(route_or_null))) return rc;
+  if (misaligned(x) || misaligned(w_router) || misaligned(out) || misaligned(ws) ||
+      (router_bias && misaligned(router_bias)))
+    return MOE_ERR_MISALIGNED;
+  const Layout L = layout_of(desc);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* base = reinterpret_cast<char*>(ws);
+  moe_route_out r;
+  if (route_or_null) {
+    r = *route_or_null;
+  } else {
+    r.topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
+    r.topk_w = reinterpret_cast<float*>(base + L.w);
+    r.counts = reinterpret_cast<int32_t*>(base + L.counts);
+    r.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    r.sorted_idx = reinterpret_cast<int32_t*>(base + L.sorted);
+    r.inv_pos = reinterpret_cast<int32_t*>(base + L.inv);
+    r.block_map = reinterpret_cast<int32_t*>(base + L.bmap);
+    r.n_tiles = reinterpret_cast<int32_t*>(base + L.ntiles);
+  }
+  void* h = base + L.h;
+  float* y = reinterpret_cast<float*>(base + L.y);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) return rc;
+  int tiles = 0;
+  if (host_sync) {
+    int32_t nt = 0;
+    if (hipMemcpyAsync(&nt, r.n_tiles, sizeof(nt), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    if (nt <= 0 || nt > max_tiles_of(desc)) return MOE_ERR_HIP;  // routing produced no valid block map
+    tiles = nt;
+  }
+  GemmWeights gu, dn;
+  gu.q = w_gate_up;
+  gu.qs = shared_gate_up;
+  dn.q = w_down;
+  dn.qs = shared_down;
+  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles))) return rc;
+  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, dn, &r, y, s, tiles))) return rc;
+  return do_combine(desc, y, &r, out, s);
 }
 
 }  // namespace
@@ -216,7 +300,10 @@ int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, con
   if (misaligned(a) || misaligned(c) || misaligned(route->sorted_idx) || misaligned(route->block_map) ||
       misaligned(route->n_tiles))
     return MOE_ERR_MISALIGNED;
-  return do_gemm(desc, mode, a, w, w_shared, route, c, reinterpret_cast<hipStream_t>(stream));
+  GemmWeights gw;
+  gw.q = w;
+  gw.qs = w_shared;
+  return do_gemm(desc, mode, a, gw, route, c, reinterpret_cast<hipStream_t>(stream));
 }
 
 int moe_combine(const moe_layer_desc* desc, const float* y, const moe_route_out* route, float* out, void* stream) {
@@ -233,46 +320,64 @@ int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint1
                       const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
                       const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
                       const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward(desc, x, w_router, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
+                       route_or_null, ws, ws_bytes, stream, false);
+}
+
+int moe_layer_forward_host_sync(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
+                                const float* router_bias, const moe_q4_tensor* w_gate_up,
+                                const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
+                                const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward(desc, x, w_router, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
+                       route_or_null, ws, ws_bytes, stream, true);
+}
+
+int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null, uint16_t* out, void* stream) {
+  if (!w || !w->codes || !w->scales || !w->biases || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->n_exp < 0 || w->N < 0 || w->K < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->K % MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (misaligned(w->codes) || misaligned(w->scales) || misaligned(w->biases) || misaligned(out) ||
+      (counts_or_null && misaligned(counts_or_null)))
+    return MOE_ERR_MISALIGNED;
+  if (w->n_exp == 0 || w->N == 0 || w->K == 0) return MOE_OK;
+  // one expert's weights and its grid stay inside 32-bit indexing
+  if ((int64_t)w->N * w->K >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  DequantArgs d;
+  d.codes = w->codes;
+  d.scales = w->scales;
+  d.biases = w->biases;
+  d.counts = counts_or_null;
+  d.out = out;
+  d.n_exp = w->n_exp;
+  d.N = w->N;
+  d.K = w->K;
+  return hip_status(launch_dequant(d, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_gemm_bf16(const moe_layer_desc* desc, int mode, const void* a, const moe_bf16_tensor* w,
+                          const moe_bf16_tensor* w_shared, const moe_route_out* route, void* c, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
+  if (mode != MOE_GEMM_GATE_UP_SWIGLU && mode != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
   if (desc->T == 0) return MOE_OK;
-  if (!x || !w_router || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
-  if ((rc = check_q4(w_gate_up, desc->E, 2 * desc->I, desc->H))) return rc;
-  if ((rc = check_q4(w_down, desc->E, desc->H, desc->I))) return rc;
+  if (!a || !c || !route || !route->sorted_idx || !route->block_map || !route->n_tiles)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int N = mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 * desc->I : desc->H;
+  const int K = mode == MOE_GEMM_GATE_UP_SWIGLU ? desc->H : desc->I;
+  if ((rc = check_bf16(w, desc->E, N, K))) return rc;
   if (desc->has_shared) {
-    if ((rc = check_q4(shared_gate_up, 1, 2 * desc->I, desc->H))) return rc;
-    if ((rc = check_q4(shared_down, 1, desc->H, desc->I))) return rc;
+    if ((rc = check_bf16(w_shared, 1, N, K))) return rc;
   } else {
-    shared_gate_up = shared_down = nullptr;
+    w_shared = nullptr;
   }
-  if (route_or_null && (rc = check_route_out(route_or_null))) return rc;
-  if (misaligned(x) || misaligned(w_router) || misaligned(out) || misaligned(ws) ||
-      (router_bias && misaligned(router_bias)))
+  if (misaligned(a) || misaligned(c) || misaligned(route->sorted_idx) || misaligned(route->block_map) ||
+      misaligned(route->n_tiles))
     return MOE_ERR_MISALIGNED;
-  const Layout L = layout_of(desc);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-
-  char* base = reinterpret_cast<char*>(ws);
-  moe_route_out r;
-  if (route_or_null) {
-    r = *route_or_null;
-  } else {
-    r.topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
-    r.topk_w = reinterpret_cast<float*>(base + L.w);
-    r.counts = reinterpret_cast<int32_t*>(base + L.counts);
-    r.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-    r.sorted_idx = reinterpret_cast<int32_t*>(base + L.sorted);
-    r.inv_pos = reinterpret_cast<int32_t*>(base + L.inv);
-    r.block_map = reinterpret_cast<int32_t*>(base + L.bmap);
-    r.n_tiles = reinterpret_cast<int32_t*>(base + L.ntiles);
-  }
-  void* h = base + L.h;
-  float* y = reinterpret_cast<float*>(base + L.y);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) return rc;
-  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, w_gate_up, shared_gate_up, &r, h, s))) return rc;
-  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, w_down, shared_down, &r, y, s))) return rc;
-  return do_combine(desc, y, &r, out, s);
+  GemmWeights gw;
+  gw.bf = w->w;
+  gw.bfs = w_shared ? w_shared->w : nullptr;
+  return do_gemm(desc, mode, a, gw, route, c, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

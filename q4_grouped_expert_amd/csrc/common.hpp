@@ -61,6 +61,8 @@ struct GemmArgs {
   const uint8_t* s_codes;   // shared expert [N][Kdim/2] (or null)
   const uint16_t* s_scales;
   const uint16_t* s_biases;
+  const uint16_t* wbf;      // unfused variant: bf16 weights [E][N][Kdim] (codes unused), else null
+  const uint16_t* s_wbf;    // and the shared expert's [N][Kdim]
   const int32_t* sorted_idx;
   const int32_t* block_map;
   const int32_t* n_tiles;
@@ -72,6 +74,18 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
+
+// Unfused variant, step 1: w_bf16[e] = bf16(fma(q, scale, bias)) for every
+// expert e < n_exp with counts[e] > 0 (all of them when counts is null).
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  const int32_t* counts;
+  uint16_t* out;
+  int n_exp, N, K;
+};
+hipError_t launch_dequant(const DequantArgs& d, hipStream_t stream);
 
 struct CombineArgs {
   const float* y;

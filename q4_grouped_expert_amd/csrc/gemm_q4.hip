@@ -72,8 +72,16 @@ constexpr int kMaxGroups = kMaxGroupsPerRow;  // scale/bias groups per weight ro
 // 16 lanes over 64 banks per cycle.  An involution: swz(r, swz(r, c)) == c.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
+// Weight registers of one stage and lane: 16 codes per subtile (8 bytes), or
+// with bf16 weights in memory the 16 bf16 values themselves (two 16-byte
+// loads per subtile).
+template <bool kBf16W>
 struct BRegs {
   u32x2 c[NS];
+};
+template <>
+struct BRegs<true> {
+  u32x4 c[NS][2];
 };
 
 // Per-workgroup state shared by every subtile-count instantiation.
@@ -91,7 +99,7 @@ struct TileCtx {
   bool jval[NS];
 };
 
-template <bool kGateUp, int MSUB>
+template <bool kGateUp, bool kBf16W, int MSUB>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, uint16_t* __restrict__ A0,
                                           uint16_t* __restrict__ A1, uint16_t* __restrict__ Ssh,
                                           uint16_t* __restrict__ Bsh) {
@@ -125,7 +133,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   }
 
   f32x4 acc[MSUB][NS];  // first written by the k-step-0 MFMAs of stage 0
-  BRegs bq[2];          // codes of two consecutive stages
+  BRegs<kBf16W> bq[2];  // weights of two consecutive stages
+  constexpr int kLoadsB = kBf16W ? 2 * NS : NS;  // weight loads per wave per stage
   bf16x8 bf[NS][2];     // dequantized B fragments of the current stage
 
   auto dma_a = [&](uint16_t* slot, int kt) {
@@ -135,20 +144,32 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
           t.a_rs, (__attribute__((address_space(3))) void*)(slot + (ROWS_PER_DMA * i + 8 * wave) * BK), 16, adoff[i],
           kt * BK * 2, 0, 0);
   };
-  auto load_b = [&](BRegs& q, int kt) {
+  auto load_b = [&](BRegs<kBf16W>& q, int kt) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      q.c[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.c_rs, t.c_off[j], kt * 32, 0));
+    for (int j = 0; j < NS; ++j) {
+      if constexpr (kBf16W) {
+        q.c[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t.c_rs, t.c_off[j], kt * 128, 0));
+        q.c[j][1] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t.c_rs, t.c_off[j], kt * 128 + 16, 0));
+      } else {
+        q.c[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.c_rs, t.c_off[j], kt * 32, 0));
+      }
+    }
   };
   // Dequantize stage kt's codes into bf, with each subtile's scale and bias
   // from the tile's LDS tables.
-  auto dequant = [&](const BRegs& q, int kt) {
+  auto dequant = [&](const BRegs<kBf16W>& q, int kt) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int idx = t.sb_row[j] * gpr + 8 * ((kt >> 3) ^ t.sb_f[j]) + (kt & 7);
-      const float sv = bf16_bits_to_f32(Ssh[idx]), bv = bf16_bits_to_f32(Bsh[idx]);
-      bf[j][0] = dequant8(q.c[j][0], sv, bv);
-      bf[j][1] = dequant8(q.c[j][1], sv, bv);
+      if constexpr (kBf16W) {
+        bf[j][0] = __builtin_bit_cast(bf16x8, q.c[j][0]);
+        bf[j][1] = __builtin_bit_cast(bf16x8, q.c[j][1]);
+      } else {
+        const int idx = t.sb_row[j] * gpr + 8 * ((kt >> 3) ^ t.sb_f[j]) + (kt & 7);
+        const float sv = bf16_bits_to_f32(Ssh[idx]), bv = bf16_bits_to_f32(Bsh[idx]);
+        bf[j][0] = dequant8(q.c[j][0], sv, bv);
+        bf[j][1] = dequant8(q.c[j][1], sv, bv);
+      }
     }
   };
   // The tile's scales and biases for the whole reduction: one or two
@@ -192,7 +213,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   // memory access, so the wait before each barrier can count them.
   const int nk = t.nk;
   const int last = nk - 1;
-  dma_sb();
+  if constexpr (!kBf16W) dma_sb();
   dma_a(A0, 0);
   load_b(bq[0], 0);
   load_b(bq[1], min(1, last));
@@ -209,7 +230,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   //    their operands), wait until only this stage's NS code loads are in
   //    flight (so the DMA of stage kt+1 has landed) and meet at the barrier
   //    (a plain s_barrier: a fenced one would drain every outstanding load).
-  auto stage = [&](auto first, int kt, BRegs& qown, const BRegs& qnext, const uint16_t* Ab, uint16_t* Anext) {
+  auto stage = [&](auto first, int kt, BRegs<kBf16W>& qown, const BRegs<kBf16W>& qnext, const uint16_t* Ab,
+                   uint16_t* Anext) {
     // The loads for later stages are spread over the subtile regions (DMA i
     // in region i, the code loads in the region after the last DMA), so
     // their issue overlaps this wave's MFMAs; the DMAs still come first.
@@ -249,7 +271,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
     if constexpr (ADMA >= MSUB) load_b(qown, min(kt + 2, last));
     // the last stage dequantizes its own codes again (clamped), unused
     dequant(qnext, min(kt + 1, last));
-    wait_vmcnt<NS>();
+    wait_vmcnt<kLoadsB>();
     __builtin_amdgcn_s_barrier();
   };
   const std::integral_constant<bool, true> kFirst;
@@ -308,7 +330,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, u
   }
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kBf16W>
 __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   // activation ring: two stages of [256 rows][64] bf16
   __shared__ __attribute__((aligned(16))) uint16_t A0[BM * BK];
@@ -352,7 +374,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
     scl = g.s_scales;
     bia = g.s_biases;
   }
-  t.c_rs = make_rsrc(codes, (uint32_t)g.N * cpr);
+  // bf16 weights in memory (the unfused variant): one row is Kd * 2 bytes
+  const uint32_t wrow = kBf16W ? (uint32_t)Kd * 2u : cpr;
+  if (kBf16W) t.c_rs = make_rsrc(e < g.E ? g.wbf + (size_t)e * g.N * Kd : g.s_wbf, (uint32_t)g.N * wrow);
+  else t.c_rs = make_rsrc(codes, (uint32_t)g.N * cpr);
   t.s_rs = make_rsrc(scl, (uint32_t)g.N * gpr * 2u);
   t.b_rs = make_rsrc(bia, (uint32_t)g.N * gpr * 2u);
   const uint32_t a_rows = kGateUp ? (uint32_t)g.T : (uint32_t)(g.R + g.T);
@@ -372,7 +397,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
       t.jval[j] = v;
       t.ocol[j] = row + ln;
       const uint32_t r = v ? (j < NS / 2 ? 0 : g.I) + row + ln : 0;
-      t.c_off[j] = r * cpr + 8u * lg;
+      t.c_off[j] = r * wrow + (kBf16W ? 32u : 8u) * lg;
       // scale/bias tables: rows 0..63 = gate rows nb*64.., 64..127 = up rows
       t.sb_row[j] = (j < NS / 2 ? 0 : BN / 2) + wave * (WN / 2) + 16 * jj + ln;
     }
@@ -386,7 +411,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
       t.jval[j] = c < g.N;
       t.ocol[j] = c + ln;
       const uint32_t r = t.jval[j] ? c + ln : 0;
-      t.c_off[j] = r * cpr + 8u * lg;
+      t.c_off[j] = r * wrow + (kBf16W ? 32u : 8u) * lg;
       t.sb_row[j] = wave * WN + 16 * j + ln;
     }
     // one contiguous range of 128 rows, split in two halves of 64
@@ -404,22 +429,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
 
   const int msub = (t.nrows + 15) >> 4;
   switch (msub) {
-    case 1: tile_body<kGateUp, 1>(g, t, A0, A1, Ssh, Bsh); break;
-    case 2: tile_body<kGateUp, 2>(g, t, A0, A1, Ssh, Bsh); break;
-    case 3: tile_body<kGateUp, 3>(g, t, A0, A1, Ssh, Bsh); break;
-    case 4: tile_body<kGateUp, 4>(g, t, A0, A1, Ssh, Bsh); break;
-    case 5: tile_body<kGateUp, 5>(g, t, A0, A1, Ssh, Bsh); break;
-    case 6: tile_body<kGateUp, 6>(g, t, A0, A1, Ssh, Bsh); break;
-    case 7: tile_body<kGateUp, 7>(g, t, A0, A1, Ssh, Bsh); break;
-    case 8: tile_body<kGateUp, 8>(g, t, A0, A1, Ssh, Bsh); break;
-    case 9: tile_body<kGateUp, 9>(g, t, A0, A1, Ssh, Bsh); break;
-    case 10: tile_body<kGateUp, 10>(g, t, A0, A1, Ssh, Bsh); break;
-    case 11: tile_body<kGateUp, 11>(g, t, A0, A1, Ssh, Bsh); break;
-    case 12: tile_body<kGateUp, 12>(g, t, A0, A1, Ssh, Bsh); break;
-    case 13: tile_body<kGateUp, 13>(g, t, A0, A1, Ssh, Bsh); break;
-    case 14: tile_body<kGateUp, 14>(g, t, A0, A1, Ssh, Bsh); break;
-    case 15: tile_body<kGateUp, 15>(g, t, A0, A1, Ssh, Bsh); break;
-    default: tile_body<kGateUp, 16>(g, t, A0, A1, Ssh, Bsh); break;
+    case 1: tile_body<kGateUp, kBf16W, 1>(g, t, A0, A1, Ssh, Bsh); break;
+    case 2: tile_body<kGateUp, kBf16W, 2>(g, t, A0, A1, Ssh, Bsh); break;
+    case 3: tile_body<kGateUp, kBf16W, 3>(g, t, A0, A1, Ssh, Bsh); break;
+    case 4: tile_body<kGateUp, kBf16W, 4>(g, t, A0, A1, Ssh, Bsh); break;
+    case 5: tile_body<kGateUp, kBf16W, 5>(g, t, A0, A1, Ssh, Bsh); break;
+    case 6: tile_body<kGateUp, kBf16W, 6>(g, t, A0, A1, Ssh, Bsh); break;
+    case 7: tile_body<kGateUp, kBf16W, 7>(g, t, A0, A1, Ssh, Bsh); break;
+    case 8: tile_body<kGateUp, kBf16W, 8>(g, t, A0, A1, Ssh, Bsh); break;
+    case 9: tile_body<kGateUp, kBf16W, 9>(g, t, A0, A1, Ssh, Bsh); break;
+    case 10: tile_body<kGateUp, kBf16W, 10>(g, t, A0, A1, Ssh, Bsh); break;
+    case 11: tile_body<kGateUp, kBf16W, 11>(g, t, A0, A1, Ssh, Bsh); break;
+    case 12: tile_body<kGateUp, kBf16W, 12>(g, t, A0, A1, Ssh, Bsh); break;
+    case 13: tile_body<kGateUp, kBf16W, 13>(g, t, A0, A1, Ssh, Bsh); break;
+    case 14: tile_body<kGateUp, kBf16W, 14>(g, t, A0, A1, Ssh, Bsh); break;
+    case 15: tile_body<kGateUp, kBf16W, 15>(g, t, A0, A1, Ssh, Bsh); break;
+    default: tile_body<kGateUp, kBf16W, 16>(g, t, A0, A1, Ssh, Bsh); break;
   }
 }
 
@@ -429,13 +454,19 @@ int grid_blocks(int max_tiles, int nN) { return (max_tiles + kXcds - 1) / kXcds 
 
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_q4_kernel<false>, dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  if (g.wbf)
+    hipLaunchKernelGGL((gemm_q4_kernel<false, true>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_q4_kernel<false, false>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.I + BN / 2 - 1) / (BN / 2);
-  hipLaunchKernelGGL(gemm_q4_kernel<true>, dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  if (g.wbf)
+    hipLaunchKernelGGL((gemm_q4_kernel<true, true>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_q4_kernel<true, false>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI that need no GPU: the library loads, exports
-every function include/moe_q4.h declares, and every status code that the
+every function include/*.h declares, and every status code that the
 argument checks can return comes back before any HIP call."""
 
 import ctypes
@@ -12,20 +12,21 @@ import pytest
 from q4_grouped_expert_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
 MIS = 0x10008
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 8
+    assert len(HEADERS) == 2 and len(names) == 11
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -163,3 +164,41 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     # bf16 and approximate logits [T][E] fp32
     assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == (
         64 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 4096 * 256 * 4)
+
+
+def test_ablation_entry_points_argument_errors():
+    L = B.lib()
+    d = B.layer_desc(64, 256, 128, 16, 4)
+    r = B.RouteOutDesc(A, A, A, A, A, A, A, A)
+    w = q4(16, 256, 128)
+    # dequant: pointers, group size, alignment
+    assert L.moe_dequant_q4_to_bf16(None, None, A, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dequant_q4_to_bf16(ctypes.byref(w), None, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dequant_q4_to_bf16(ctypes.byref(q4(2, 8, 96)), None, A, None) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert L.moe_dequant_q4_to_bf16(ctypes.byref(w), MIS, A, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_dequant_q4_to_bf16(ctypes.byref(w), None, MIS, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_dequant_q4_to_bf16(ctypes.byref(q4(0, 256, 128)), None, A, None) == B.MOE_OK  # nothing to do
+    # bf16 GEMM: mode, shapes, shared expert, alignment
+    bw = B.Bf16Desc(A, 16, 256, 256)  # gate/up of H=256, I=128: N = 2I = 256, K = H = 256
+    bs = B.Bf16Desc(A, 1, 256, 256)
+    assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 7, A, ctypes.byref(bw), ctypes.byref(bs), ctypes.byref(r), A,
+                                   None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 0, A, ctypes.byref(bw), None, ctypes.byref(r), A,
+                                   None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 1, A, ctypes.byref(bw), ctypes.byref(bs), ctypes.byref(r), A,
+                                   None) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 0, A, ctypes.byref(B.Bf16Desc(MIS, 16, 256, 256)),
+                                   ctypes.byref(bs), ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_grouped_gemm_bf16(ctypes.byref(B.layer_desc(0, 256, 128, 16, 4)), 0, A, ctypes.byref(bw),
+                                   ctypes.byref(bs), ctypes.byref(r), A, None) == B.MOE_OK
+    # host-synchronizing layer: the same checks as moe_layer_forward
+    gu, dn, sgu, sdn = q4(16, 256, 256), q4(16, 256, 128), q4(1, 256, 256), q4(1, 256, 128)
+    need = B.moe_workspace_size(d, 1)
+    call = lambda desc, ws_bytes=need, out=A: L.moe_layer_forward_host_sync(  # noqa: E731
+        ctypes.byref(desc), A, A, None, ctypes.byref(gu), ctypes.byref(dn), ctypes.byref(sgu), ctypes.byref(sdn),
+        out, None, A, ws_bytes, None)
+    assert call(d, need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, out=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(B.layer_desc(64, 100, 128, 16, 4)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
