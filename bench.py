@@ -108,6 +108,8 @@ def main() -> int:
         return 2
     shape = gen.WORKLOADS[args.workload]
     B.lib()  # raises if the HIP library is missing
+    if args.workload.startswith("decode"):
+        return run_decode(args, shape, torch, B, gen)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = gen.make_layer(shape)
@@ -288,6 +290,67 @@ def main() -> int:
         res["cpu_baseline"] = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                                "sample": f"first {S} of the {T} tokens, whole layer (routing, dequant of every "
                                          f"expert with rows, SwiGLU FFN, combine), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_decode(args, shape, torch, B, gen):
+    """The decode-shape layer (moe_decode_forward, at most 16 tokens): layer
+    tokens/s and, as its roofline, the HBM bytes the call must move (the Q4
+    weights of every expert with rows plus the shared expert, x and out) over
+    the layer's time."""
+    import numpy as np
+
+    from q4_grouped_expert_amd.device import DeviceLayer
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = gen.make_layer(shape)
+    dl = DeviceLayer(inp, dev)
+    T, H, I, E, K = shape.T, shape.H, shape.I, shape.E, shape.K
+    route = dl.new_route(T)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    dl.decode_router()  # the prepared router copy is per model, outside the step
+    for _ in range(args.warmup):
+        dl.decode(dl.x, out, route, stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        dl.decode(dl.x, out, route, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    layer_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    counts = route["counts"].cpu().numpy()
+    n_ne = int((counts > 0).sum()) + (1 if dl.has_shared else 0)
+    wbytes = n_ne * ((2 * I * H + H * I) // 2 + (2 * I * (H // 64) + H * (I // 64)) * 4)
+    hbm_bytes = wbytes + T * H * 2 + T * H * 4
+    achieved = hbm_bytes / (layer_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MoE decode layer tokens/s (1-16 tokens per call)",
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: T={T} H={H} I={I} E={E} top-{K}"
+                               f"{' + 1 shared' if dl.has_shared else ''}, decode path", "tokens": T,
+                   "seed": shape.seed, "norm_topk": 1},
+        "roofline": {"kernel": "decode layer (router, grouping, split-reduction GEMVs, combine)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": hbm_bytes, "avg_launch_ms": round(layer_ms, 4)},
+        "experts_read": n_ne,
+    }
     print(json.dumps(res), flush=True)
     return 0
 

@@ -1,0 +1,50 @@
+/* libmoeq4: the decode-shape MoE layer, at most 16 tokens per call.
+ *
+ * Decode produces one token per sequence at a time, so its cost is the
+ * weight bytes moved per token ("Perplexity Lily 오픈소스 공개",
+ * alltoptrend.co.kr, section 6; "Apple silicon용 Lily, Qwen 추론 최적화",
+ * aitrends.kr, section "Decode의 토큰 단위 최적화").  This path computes
+ * exactly what moe_layer_forward computes for the same tokens (the same
+ * routing rule and sequential fp32 logits, the same bf16 weights, fp32
+ * accumulation) with kernels sized for a handful of rows: an exact router
+ * over all experts and a one-workgroup grouping step; for a single token the
+ * expert FFN runs as GEMVs that split the reduction over the waves of a
+ * workgroup, from two tokens on as the tiled grouped GEMM.  Only the weights
+ * of the chosen experts (plus the shared expert) are read.
+ *
+ * Conventions are those of moe_q4.h.
+ */
+#ifndef MOE_Q4_DECODE_H
+#define MOE_Q4_DECODE_H
+
+#include "moe_q4.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_MAX_TOKENS 16
+
+/* Write the router matrix once per model in the layout the decode router
+ * reads: w_router_pm[h/4][e][i] = (fp32) w_router[e][4*(h/4) + i], i < 4
+ * (E * H fp32, device, caller-owned).  desc supplies H and E (T unused). */
+int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, float* w_router_pm,
+                              void* stream);
+
+/* The layer for 1 <= T <= MOE_DECODE_MAX_TOKENS tokens (T == 0: no-op):
+ * routing (every expert's logit as one fp32 chain over h, top_k by (logit
+ * descending, expert ascending), weights as in moe_layer_forward), grouping
+ * (counts, offsets, stable sorted_idx / inv_pos, a block map with one tile per
+ * expert with rows and then the shared expert's), gate/up + SwiGLU, down and
+ * the combine, all on `stream`.  w_router_pm: from
+ * moe_decode_router_prepare.  Other arguments and the workspace
+ * (moe_workspace_size(desc, 1) bytes) as for moe_layer_forward. */
+int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+                       const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
+                       const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
+                       const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_Q4_DECODE_H */

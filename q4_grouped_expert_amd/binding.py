@@ -1,5 +1,5 @@
-"""Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h and
-include/moe_q4_ablation.h).
+"""Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h,
+include/moe_q4_ablation.h and include/moe_q4_decode.h).
 
 Argument marshalling only: torch tensors supply device memory and the HIP
 stream, every step of the layer runs in the library's HIP kernels.  There is
@@ -72,7 +72,13 @@ SIGNATURES = {
                                                    ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                                    ctypes.POINTER(Q4Desc), c_p, ctypes.POINTER(RouteOutDesc), c_p,
                                                    ctypes.c_size_t, c_p]),
+    # the decode-shape layer (moe_q4_decode.h)
+    "moe_decode_router_prepare": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p]),
+    "moe_decode_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
+                                          ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
+                                          c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
 }
+MOE_DECODE_MAX_TOKENS = 16
 
 _lib = None
 
@@ -207,3 +213,17 @@ def moe_grouped_gemm_bf16(desc, mode, a, w: Bf16Desc, w_shared: Optional[Bf16Des
     _chk("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
         ctypes.byref(desc), mode, _ptr(a), ctypes.byref(w),
         ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _stream(stream)))
+
+
+def moe_decode_router_prepare(desc, w_router, w_router_pm, stream=None):
+    _chk("moe_decode_router_prepare", lib().moe_decode_router_prepare(ctypes.byref(desc), _ptr(w_router),
+                                                                      _ptr(w_router_pm), _stream(stream)))
+
+
+def moe_decode_forward(desc, x, w_router_pm, router_bias, w_gate_up: Q4Desc, w_down: Q4Desc,
+                       shared_gate_up: Optional[Q4Desc], shared_down: Optional[Q4Desc], out,
+                       route: Optional[RouteOutDesc], ws, ws_bytes, stream=None):
+    byref = lambda d: ctypes.byref(d) if d is not None else None  # noqa: E731
+    _chk("moe_decode_forward", lib().moe_decode_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router_pm), _ptr(router_bias), byref(w_gate_up), byref(w_down),
+        byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes, _stream(stream)))

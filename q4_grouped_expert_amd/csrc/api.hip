@@ -6,12 +6,16 @@
 
 #include "common.hpp"
 #include "moe_q4_ablation.h"
+#include "moe_q4_decode.h"
 
 using namespace moeq4;
 
 namespace {
 
 constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
+// Tokens up to which the decode path runs the expert FFN as split-reduction
+// GEMVs instead of the tiled grouped GEMM.
+constexpr int kDecodeGemvMaxTokens = 1;
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -119,7 +123,7 @@ struct GemmWeights {
 // tiles > 0: launch exactly that many tiles (known on the host) instead of
 // the bound max_tiles_of(d).
 int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights& w, const moe_route_out* r, void* c,
-            hipStream_t s, int tiles = 0) {
+            hipStream_t s, int tiles = 0, bool decode = false) {
   GemmArgs g;
   g.a = reinterpret_cast<const uint16_t*>(a);
   g.codes = w.q ? w.q->codes : nullptr;
@@ -143,11 +147,11 @@ int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights&
   if (mode == MOE_GEMM_GATE_UP_SWIGLU) {
     g.N = 2 * d->I;
     g.Kdim = d->H;
-    return hip_status(launch_gemm_gate_up(g, s));
+    return hip_status(decode ? launch_decode_gemv(g, true, s) : launch_gemm_gate_up(g, s));
   }
   g.N = d->H;
   g.Kdim = d->I;
-  return hip_status(launch_gemm_down(g, s));
+  return hip_status(decode ? launch_decode_gemv(g, false, s) : launch_gemm_down(g, s));
 }
 
 int do_combine(const moe_layer_desc* d, const float* y, const moe_route_out* r, float* out, hipStream_t s) {
@@ -175,12 +179,16 @@ int check_bf16(const moe_bf16_tensor* t, int n_exp, int N, int K) {
 
 // The layer for one chunk.  host_sync: after routing, copy n_tiles to the
 // host, wait for the stream and size the GEMM grids from it.
+// decode_wf: the decode path (T <= 16) with the prepared fp32 router copy;
+// w_router is then unused.
 int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                   const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                   const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null, void* ws,
-                  size_t ws_bytes, void* stream, bool host_sync) {
+                  size_t ws_bytes, void* stream, bool host_sync, const float* decode_wf = nullptr) {
   int rc = check_desc(desc);
   if (rc) return rc;
+  const bool decode = decode_wf != nullptr;
+  if (decode && desc->T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (desc->T == 0) return MOE_OK;
   if (!x || !w_router || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if ((rc = check_q4(w_gate_up, desc->E, 2 * desc->I, desc->H))) return rc;
@@ -199,6 +207,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   moe_route_out r;
   if (route_or_null) {
     r = *route_or_null;
@@ -214,8 +223,23 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   }
   void* h = base + L.h;
   float* y = reinterpret_cast<float*>(base + L.y);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) return rc;
+  if (decode) {
+    DecodeRouteArgs a;
+    a.x = x;
+    a.wf = decode_wf;
+    a.router_bias = router_bias;
+    a.logits = reinterpret_cast<float*>(base + L.hist);  // the routing scratch holds T*E fp32 and more
+    a.T = desc->T;
+    a.H = desc->H;
+    a.E = desc->E;
+    a.K = desc->top_k;
+    a.norm_topk = desc->norm_topk;
+    a.has_shared = desc->has_shared;
+    a.out = r;
+    if ((rc = hip_status(launch_decode_route(a, s)))) return rc;
+  } else if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) {
+    return rc;
+  }
   int tiles = 0;
   if (host_sync) {
     int32_t nt = 0;
@@ -229,8 +253,11 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   gu.qs = shared_gate_up;
   dn.q = w_down;
   dn.qs = shared_down;
-  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles))) return rc;
-  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, dn, &r, y, s, tiles))) return rc;
+  // decode: the split-reduction GEMV for a single token, the tiled GEMM from
+  // two tokens on (measured faster there on MI355X)
+  const bool gemv = decode && desc->T <= kDecodeGemvMaxTokens;
+  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv))) return rc;
+  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv))) return rc;
   return do_combine(desc, y, &r, out, s);
 }
 
@@ -331,6 +358,27 @@ int moe_layer_forward_host_sync(const moe_layer_desc* desc, const uint16_t* x, c
                                 void* ws, size_t ws_bytes, void* stream) {
   return layer_forward(desc, x, w_router, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
                        route_or_null, ws, ws_bytes, stream, true);
+}
+
+int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, float* w_router_pm,
+                              void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!w_router || !w_router_pm) return MOE_ERR_INVALID_ARGUMENT;
+  if (misaligned(w_router) || misaligned(w_router_pm)) return MOE_ERR_MISALIGNED;
+  return hip_status(launch_decode_prep(w_router, desc->H, desc->E, w_router_pm, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+                       const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
+                       const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
+                       const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
+  if (!w_router_pm) return MOE_ERR_INVALID_ARGUMENT;
+  if (misaligned(w_router_pm)) return MOE_ERR_MISALIGNED;
+  // the bf16 router matrix is not read on this path; the prepared copy stands
+  // in for it in the shared argument checks
+  return layer_forward(desc, x, reinterpret_cast<const uint16_t*>(w_router_pm), router_bias, w_gate_up, w_down,
+                       shared_gate_up, shared_down, out, route_or_null, ws, ws_bytes, stream, false, w_router_pm);
 }
 
 int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null, uint16_t* out, void* stream) {

@@ -77,6 +77,23 @@ class DeviceLayer:
                             self.s_down.desc if self.has_shared else None, out, rd, self.ws, self.ws_bytes,
                             stream)
 
+    def decode_router(self) -> torch.Tensor:
+        """The fp32 piece-major router copy the decode path reads (made once)."""
+        if getattr(self, "_wf", None) is None:
+            s = self.shape
+            self._wf = torch.empty((s.H // 4, s.E, 4), dtype=torch.float32, device=self.device)
+            B.moe_decode_router_prepare(self.desc(0), self.w_router, self._wf)
+        return self._wf
+
+    def decode(self, x: torch.Tensor, out: torch.Tensor, route: Optional[dict] = None, stream=None):
+        """The decode-shape layer for at most 16 tokens."""
+        T = x.shape[0]
+        assert T <= min(self.chunk, B.MOE_DECODE_MAX_TOKENS)
+        rd = B.route_desc(route) if route is not None else None
+        B.moe_decode_forward(self.desc(T), x, self.decode_router(), self.router_bias, self.gate_up.desc,
+                             self.down.desc, self.s_gate_up.desc if self.has_shared else None,
+                             self.s_down.desc if self.has_shared else None, out, rd, self.ws, self.ws_bytes, stream)
+
     def forward(self, x: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, routes=None,
                 stream=None) -> torch.Tensor:
         """The whole prompt in bounded chunks through the one workspace."""

@@ -60,6 +60,10 @@ WORKLOADS = {
     "prefill4096": LayerShape("prefill4096", T=4096, H=2048, I=512, E=256, K=8, seed=1003),
     "skew2048": LayerShape("skew2048", T=2048, H=2048, I=512, E=256, K=8, zipf_s=1.2, seed=1004),
     "long16384": LayerShape("long16384", T=16384, H=2048, I=512, E=256, K=8, chunk=4096, seed=1005),
+    # decode-shape calls of the same layer (one token per sequence, 1-16 sequences)
+    "decode1": LayerShape("decode1", T=1, H=2048, I=512, E=256, K=8, seed=1101),
+    "decode4": LayerShape("decode4", T=4, H=2048, I=512, E=256, K=8, seed=1104),
+    "decode16": LayerShape("decode16", T=16, H=2048, I=512, E=256, K=8, seed=1116),
 }
 
 # Stream ids for each tensor of a layer.

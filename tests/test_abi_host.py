@@ -26,7 +26,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(HEADERS) == 2 and len(names) == 11
+    assert len(HEADERS) == 3 and len(names) == 13
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -201,4 +201,25 @@ def test_ablation_entry_points_argument_errors():
     assert call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
     assert call(d, out=MIS) == B.MOE_ERR_MISALIGNED
     assert call(B.layer_desc(64, 100, 128, 16, 4)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
+
+
+def test_decode_entry_points_argument_errors():
+    L = B.lib()
+    d = B.layer_desc(4, 256, 128, 16, 4)
+    gu, dn, sgu, sdn = q4(16, 256, 256), q4(16, 256, 128), q4(1, 256, 256), q4(1, 256, 128)
+    need = B.moe_workspace_size(d, 1)
+    assert L.moe_decode_router_prepare(ctypes.byref(d), None, A, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_decode_router_prepare(ctypes.byref(d), A, MIS, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_decode_router_prepare(ctypes.byref(B.layer_desc(4, 100, 128, 16, 4)), A, A,
+                                       None) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    call = lambda desc, wf=A, ws_bytes=need, out=A: L.moe_decode_forward(  # noqa: E731
+        ctypes.byref(desc), A, wf, None, ctypes.byref(gu), ctypes.byref(dn), ctypes.byref(sgu), ctypes.byref(sdn),
+        out, None, A, ws_bytes, None)
+    assert call(d, wf=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, wf=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    big = B.layer_desc(B.MOE_DECODE_MAX_TOKENS + 1, 256, 128, 16, 4)
+    assert call(big, ws_bytes=B.moe_workspace_size(big, 1)) == B.MOE_ERR_UNSUPPORTED_SHAPE
     assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
