@@ -140,7 +140,10 @@ int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 /* Workspace bytes needed by moe_route (ws_kind = 0: expert histograms per
  * 64-token group, E * (ceil(T/64) rounded up to 4) int32, 256 fp32
  * router-row norms, a piece-major copy of the router matrix E * H bf16 and
- * the approximate router logits T * E fp32, each piece 256-byte aligned) or moe_layer_forward (ws_kind = 1; also routing
+ * the approximate router logits as ns partial sums ns * T * E fp32, ns = 1, 2,
+ * 4 or 8 splits of the hidden axis (the most that keep the logit grid at or
+ * below 256 workgroups of 64 tokens x 64 experts), each piece 256-byte
+ * aligned) or moe_layer_forward (ws_kind = 1; also routing
  * buffers, h and y).  Host-only, pure.  Workspace contents need no
  * initialization and are overwritten. */
 int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes);

@@ -22,11 +22,14 @@ namespace moeq4 {
 //
 // Computing all T*E logits on the fp32 VALU costs 2*T*H*E flops.  Instead:
 //  1. approximate logits a[t,e] with bf16 MFMA (fp32 accumulation, any
-//     internal order);
+//     internal order), the hidden axis cut into ns equal splits whose
+//     partial sums are added in order, then the bias;
 //  2. bound both errors: |a - exact| <= da and |canonical - exact| <= dc,
 //     with sum_h |x w| <= ||x_t|| * max_e ||w_e|| =: S (Cauchy-Schwarz),
-//     da = 34 (H/32 + 1) 2^-23 S  (each 32-product MFMA step off by at most
-//     33 fp32 ulps of its inputs, for any summation order or truncation),
+//     da = 34 (H/32 + ns + 1) 2^-23 S  (each 32-product MFMA step off by at
+//     most 33 fp32 ulps of its inputs, for any summation order or
+//     truncation; each split adds at most one more step's worth, and the
+//     ns - 1 adds of partial sums one ulp of S each),
 //     dc = (H + 2) 2^-24 S  (bounds the rounding of an fp32 sum of H terms
 //     in any order, the bias add included);
 //  3. with tau = the K-th largest a[t,.], every expert outside
@@ -89,6 +92,7 @@ __device__ __forceinline__ rsrc_t rsrc_of(const void* p, uint32_t bytes) {
 // reads for 16 consecutive rows); an involution.
 __device__ __forceinline__ int rswz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
 constexpr int kLgTile = 64;  // tokens and experts per approximate-logits workgroup
+constexpr int kMaxLogitSplits = 8;  // hidden-axis splits of the approximate logits
 constexpr int kLgK = 64;     // hidden columns per stage
 // s_waitcnt that bounds only the vector-memory counter (gfx9 encoding: vmcnt
 // in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -131,18 +135,25 @@ __device__ __forceinline__ uint64_t lanes_below() {
 // the neb workgroups that share a token tile run on one XCD and share its
 // L2.  Ids past the last token tile exit at once.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb, int neb, float* __restrict__ alog) {
+__global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb, int neb, int nsplit,
+                                                           float* __restrict__ alog) {
   constexpr int kRows = 2 * kLgTile;            // token rows, then router rows
   constexpr int kSlot = kRows * kLgK;           // bf16 elements per ring slot
   __shared__ __attribute__((aligned(16))) uint16_t ring[3 * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-  const int q = blockIdx.x >> 3;
-  const int tb = (q / neb) * 8 + (blockIdx.x & 7), eb = q % neb;
+  // split of the hidden axis outermost, then the token-tile / expert-tile
+  // order described above
+  const int base = (ntb + 7) / 8 * 8 * neb;
+  const int split = blockIdx.x / base, bb = blockIdx.x - split * base;
+  const int q = bb >> 3;
+  const int tb = (q / neb) * 8 + (bb & 7), eb = q % neb;
   if (tb >= ntb) return;
   const int t0 = tb * kLgTile, e0 = eb * kLgTile;
   const int T = a.T, H = a.H, E = a.E;
+  const int nk = H / kLgK / nsplit;  // stages of this split
+  const int kbase = split * nk;      // its first stage
   const rsrc_t x_rs = rsrc_of(a.x, (uint32_t)T * H * 2u);
   const rsrc_t w_rs = rsrc_of(a.w_router, (uint32_t)E * H * 2u);
 
@@ -164,10 +175,10 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb,
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           x_rs, (__attribute__((address_space(3))) void*)(S + (16 * wave + 8 * i) * kLgK), 16, xoff[i],
-          kt * kLgK * 2, 0, 0);
+          (kbase + kt) * kLgK * 2, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_rs, (__attribute__((address_space(3))) void*)(S + (kLgTile + 16 * wave + 8 * i) * kLgK), 16, woff[i],
-          kt * kLgK * 2, 0, 0);
+          (kbase + kt) * kLgK * 2, 0, 0);
     }
   };
 
@@ -205,7 +216,6 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb,
   // the other waves at the barrier.  Past the last stage the DMAs repeat
   // the last one, keeping the count per stage fixed; no other vector-memory
   // access runs inside the loop, so the count is exact.
-  const int nk = H / kLgK;
   const int last = nk - 1;
   dma(0, 0);
   dma(1, min(1, last));
@@ -232,18 +242,19 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb,
   }
   wait_vmcnt<0>();  // no direct-to-LDS write outlives the workgroup
 
-  // approximate logits (+ bias); MFMA layout: lane holds rows 4*lg+i, column ln
+  // this split's partial sums (the selection kernel adds the splits in order,
+  // then the bias); MFMA layout: lane holds rows 4*lg+i, column ln
+  float* part = alog + (size_t)split * T * E;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = e0 + 32 * wn + 16 * j + ln;
     if (e < E) {
-      const float rb = a.router_bias ? a.router_bias[e] : 0.0f;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = t0 + 32 * wm + 16 * m + 4 * lg + i;
-          if (t < T) alog[(size_t)t * E + e] = acc[m][j][i] + rb;
+          if (t < T) part[(size_t)t * E + e] = acc[m][j][i];
         }
     }
   }
@@ -302,6 +313,7 @@ __device__ __forceinline__ void ballot_ge4(uint64_t (&m)[4], const uint32_t (&k)
 // experts, being sorted, share cache lines.  Router pieces stream P pieces
 // ahead of use in registers.
 // ---------------------------------------------------------------------------
+template <int NSPLIT>
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const float* __restrict__ alog,
                                                            const float* __restrict__ wn,
                                                            const uint16_t* __restrict__ wt,
@@ -354,13 +366,26 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
         v[j][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
       }
     }
+    // the approximate logits: the hidden-axis splits added in order (the
+    // bias follows in the candidate step)
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = t0 + TPW * wave + j;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = 4 * lane + q;
-        av[j][q] = t < T && e < E ? alog[(size_t)t * E + e] : 0.0f;
+        float v = 0.0f;
+        if (t < T && e < E) {
+          // every split's load is issued before the adds, then the partial
+          // sums are added in split order
+          float pv[NSPLIT];
+#pragma unroll
+          for (int sp = 0; sp < NSPLIT; ++sp) pv[sp] = alog[((size_t)sp * T + t) * E + e];
+          v = pv[0];
+#pragma unroll
+          for (int sp = 1; sp < NSPLIT; ++sp) v += pv[sp];
+        }
+        av[j][q] = v;
       }
     }
     float wv[MOE_MAX_EXPERTS / 64];
@@ -415,6 +440,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   // widens the candidate set.  With fewer than K lanes holding keys
   // (E < 4K) no prefix qualifies and every expert is a candidate.
   {
+    if (a.router_bias) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * lane + q < E) av[j][q] = av[j][q] + bias_s[4 * lane + q];
+    }
     uint32_t mk[TPW], th[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
         win = INFINITY;
       } else {
         const float S = xn_s[tk] * wmax_s * 1.001f;
-        const float da = 34.0f * (float)(H / 32 + 1) * 0x1p-23f * S;
+        const float da = 34.0f * (float)(H / 32 + NSPLIT + 1) * 0x1p-23f * S;
         const float dc = (float)(H + 2) * 0x1p-24f * S;
         win = 2.1f * (da + dc) + 0x1p-20f * (fabsf(tau) + 1.0f);
       }
@@ -779,6 +811,16 @@ struct RouteWs {
 };
 // expert-histogram row length: 64-token groups rounded up to 4
 int hist_row(int T) { return ((T + kHistTokens - 1) / kHistTokens + 3) & ~3; }
+// splits of the hidden axis for the approximate logits: as many as keep the
+// grid at or below one workgroup per CU (at most 8, each a whole number of
+// 64-column stages), so short prompts fill the chip
+int logit_splits(int T, int H, int E) {
+  const int ntb = (T + kLgTile - 1) / kLgTile, neb = (E + kLgTile - 1) / kLgTile;
+  const int base = (ntb + 7) / 8 * 8 * neb;
+  int ns = 1;
+  while (ns < kMaxLogitSplits && base * ns * 2 <= 256 && (H / kLgK) % (ns * 2) == 0) ns *= 2;
+  return ns;
+}
 RouteWs route_ws_layout(int T, int H, int E) {
   const size_t ng = (size_t)hist_row(T);
   RouteWs L;
@@ -786,7 +828,7 @@ RouteWs route_ws_layout(int T, int H, int E) {
   L.wn = align256(ng * (size_t)E * sizeof(int32_t));             // router row norms
   L.wt = L.wn + align256(MOE_MAX_EXPERTS * sizeof(float));        // piece-major router copy [H/8][E][8] bf16
   L.alog = L.wt + align256((size_t)E * H * sizeof(uint16_t));     // approximate logits [T][E]
-  L.total = L.alog + align256((size_t)T * E * sizeof(float));
+  L.total = L.alog + align256((size_t)logit_splits(T, H, E) * T * E * sizeof(float));
   return L;
 }
 }  // namespace
@@ -806,10 +848,17 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
-  hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb), dim3(256), 0, stream, a, ntb, neb, alog);
+  const int ns = logit_splits(a.T, a.H, a.E);
+  hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb * ns), dim3(256), 0, stream, a, ntb, neb, ns,
+                     alog);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select_kernel, dim3((a.T + kSelTokens - 1) / kSelTokens), dim3(256), 0, stream, a, alog,
-                     wn, wt, hist, ngp);
+  const dim3 sel_grid((a.T + kSelTokens - 1) / kSelTokens);
+  switch (ns) {
+    case 1: hipLaunchKernelGGL(route_select_kernel<1>, sel_grid, dim3(256), 0, stream, a, alog, wn, wt, hist, ngp); break;
+    case 2: hipLaunchKernelGGL(route_select_kernel<2>, sel_grid, dim3(256), 0, stream, a, alog, wn, wt, hist, ngp); break;
+    case 4: hipLaunchKernelGGL(route_select_kernel<4>, sel_grid, dim3(256), 0, stream, a, alog, wn, wt, hist, ngp); break;
+    default: hipLaunchKernelGGL(route_select_kernel<8>, sel_grid, dim3(256), 0, stream, a, alog, wn, wt, hist, ngp); break;
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_group_kernel, dim3(ng), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ngp, a.T, a.K, a.E,
                      a.has_shared, a.out);

@@ -141,7 +141,9 @@ def test_entry_point_argument_errors():
                        1 << 20, None) == B.MOE_ERR_MISALIGNED
     need = B.moe_workspace_size(d, 0)
     a256 = lambda n: (n + 255) // 256 * 256
-    assert need == a256(4 * 16 * 4) + 256 * 4 + a256(16 * 256 * 2) + a256(64 * 16 * 4)
+    # approximate logits in 4 hidden-axis splits (a short prompt's logit grid is
+    # split until it would pass one workgroup per CU)
+    assert need == a256(4 * 16 * 4) + 256 * 4 + a256(16 * 256 * 2) + a256(4 * 64 * 16 * 4)
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), A, need - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -161,9 +163,12 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     assert big > small
     # routing scratch: expert histograms [E][64-token groups rounded up to 4]
     # int32, 256 router-row norms, the piece-major router copy [H/8][E][8]
-    # bf16 and approximate logits [T][E] fp32
+    # bf16 and approximate logits [T][E] fp32 (4096 tokens: one split)
     assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == (
         64 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 4096 * 256 * 4)
+    # 512 tokens: 8 splits
+    assert B.moe_workspace_size(B.layer_desc(512, 2048, 512, 256, 8), 0) == (
+        8 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 8 * 512 * 256 * 4)
 
 
 def test_ablation_entry_points_argument_errors():
