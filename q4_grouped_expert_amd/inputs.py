@@ -151,3 +151,74 @@ def make_layer(shape: LayerShape, seed: Optional[int] = None) -> LayerInputs:
 
 def custom_shape(T, H, I, E, K, shared=True, zipf_s=0.0, seed=7, name="custom") -> LayerShape:
     return LayerShape(name, T=T, H=H, I=I, E=E, K=K, shared=shared, zipf_s=zipf_s, seed=seed)
+
+
+# ---- Gated DeltaNet prefill scan -------------------------------------------
+#
+# Input recipe (independent streams of one seed):
+#
+# * q, k      bf16 [T, HK, DK]  ~ N(0, 1), each (token, head) vector scaled to
+#             unit L2 norm before the bf16 rounding (the layer normalises q
+#             and k before the scan)
+# * v         bf16 [T, HV, DV]  ~ N(0, 1)
+# * alpha     fp32 [T, HV]      ~ U(0.9, 1.0)   (gate / decay per token)
+# * beta      fp32 [T, HV]      ~ U(0.05, 0.95) (write strength per token)
+# * state_in  fp32 [HV, DV, DK] ~ N(0, 0.1), or None (zeros)
+#
+# The head layout follows the hidden size of the MoE layer above (H = 2048):
+# 16 key heads and 32 value heads of dimension 128, two value heads per key
+# head.
+
+_GQ, _GK, _GV, _GA, _GB, _GS = 101, 102, 103, 104, 105, 106
+
+
+@dataclasses.dataclass(frozen=True)
+class GdnShape:
+    name: str
+    T: int
+    HK: int
+    HV: int
+    DK: int
+    DV: int
+    seed: int
+    zero_state: bool = False
+
+
+@dataclasses.dataclass
+class GdnInputs:
+    shape: GdnShape
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray
+    beta: np.ndarray
+    state_in: Optional[np.ndarray]
+
+
+GDN_WORKLOADS = {
+    "gdn_tiny": GdnShape("gdn_tiny", T=64, HK=2, HV=4, DK=64, DV=32, seed=2001),
+    "gdn512": GdnShape("gdn512", T=512, HK=16, HV=32, DK=128, DV=128, seed=2002),
+    "gdn4096": GdnShape("gdn4096", T=4096, HK=16, HV=32, DK=128, DV=128, seed=2003),
+}
+
+
+def _unit_rows(a: np.ndarray) -> np.ndarray:
+    n = np.sqrt((a.astype(np.float64) ** 2).sum(axis=-1, keepdims=True))
+    return (a / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def make_gdn(shape: GdnShape, seed: Optional[int] = None) -> GdnInputs:
+    sd = shape.seed if seed is None else seed
+    T, HK, HV, DK, DV = shape.T, shape.HK, shape.HV, shape.DK, shape.DV
+    q = bf16_bits(_unit_rows(_rng(sd, _GQ).standard_normal((T, HK, DK), dtype=np.float32)))
+    k = bf16_bits(_unit_rows(_rng(sd, _GK).standard_normal((T, HK, DK), dtype=np.float32)))
+    v = bf16_bits(_rng(sd, _GV).standard_normal((T, HV, DV), dtype=np.float32))
+    alpha = _rng(sd, _GA).uniform(0.9, 1.0, (T, HV)).astype(np.float32)
+    beta = _rng(sd, _GB).uniform(0.05, 0.95, (T, HV)).astype(np.float32)
+    st = None if shape.zero_state else (
+        _rng(sd, _GS).standard_normal((HV, DV, DK), dtype=np.float32) * np.float32(0.1))
+    return GdnInputs(shape, q, k, v, alpha, beta, st)
+
+
+def gdn_shape(T, HK, HV, DK, DV, seed=7, zero_state=False, name="custom") -> GdnShape:
+    return GdnShape(name, T=T, HK=HK, HV=HV, DK=DK, DV=DV, seed=seed, zero_state=zero_state)
