@@ -27,6 +27,79 @@ if ROOT not in sys.path:
 METRIC = "MoE prefill layer tokens/s at 4K tokens; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+# fp32 vector FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+# (the published 157.3 TFLOP/s counts packed fp32 ops, which this library does not use)
+PEAK_FP32_VALU_TFLOPS = 78.6
+def run_gdn(args, shape, torch, B, gen):
+    """The Gated DeltaNet prefill scan (gdn_prefill_scan): tokens/s and, as
+    its roofline, fp32 vector arithmetic: 7*DK flops per state row and token
+    (recall S.k: 2 DK, update alpha*S + c*k: 3 DK, output S.q: 2 DK) over the
+    kernel's time."""
+    import numpy as np
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = gen.make_gdn(shape)
+    T, HK, HV, DK, DV = shape.T, shape.HK, shape.HV, shape.DK, shape.DV
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)  # noqa: E731
+    q, k, v = u16(inp.q), u16(inp.k), u16(inp.v)
+    al = torch.from_numpy(inp.alpha).to(dev)
+    be = torch.from_numpy(inp.beta).to(dev)
+    si = torch.from_numpy(inp.state_in).to(dev) if inp.state_in is not None else None
+    o = torch.empty((T, HV, DV), dtype=torch.float32, device=dev)
+    so = torch.empty((HV, DV, DK), dtype=torch.float32, device=dev)
+    desc = B.gdn_desc(T, HK, HV, DK, DV)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.gdn_prefill_scan(desc, q, k, v, al, be, si, o, so, stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        B.gdn_prefill_scan(desc, q, k, v, al, be, si, o, so, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flop = 7.0 * DK * DV * HV * T
+    achieved = flop / (scan_ms * 1e-3) / 1e12
+    hbm = 2 * T * HK * DK * 2 + T * HV * DV * 2 + 2 * T * HV * 4 + T * HV * DV * 4 + 2 * HV * DV * DK * 4
+    res = {
+        "metric": "Gated DeltaNet prefill scan tokens/s",
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: T={T} key heads={HK} value heads={HV} DK={DK} DV={DV}, "
+                               "gated delta rule, fp32 state", "tokens": T, "seed": shape.seed},
+        "roofline": {"kernel": "gdn_scan_kernel", "bound": "alu", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 4),
+                     "traffic": load_traffic("gdn_scan", args.workload), "flop_per_launch": flop,
+                     "avg_launch_ms": round(scan_ms, 4)},
+        "hbm_bytes_algorithmic": hbm,
+        "hbm_GBs": round(hbm / (scan_ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle.gdn as G
+
+        threads = min(int(os.environ.get("OMP_NUM_THREADS") or (os.cpu_count() or 1)), os.cpu_count() or 1, HV)
+        t1 = time.perf_counter()
+        G.scan(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.state_in)
+        dt = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": round(T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"all {T} tokens, fp64 gated delta rule over {HV} heads, {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -74,7 +147,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill4096",
-                    help="prefill4096 (default), prefill512, skew2048, long16384 or tiny")
+                    help="prefill4096 (default), prefill512, skew2048, long16384, tiny; decode1, decode4, "
+                         "decode16 (decode-shape layer); gdn4096, gdn512, gdn_tiny (Gated DeltaNet prefill scan)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused_dequant", "host_sync"],
                     help="fused: the layer as built (default); unfused_dequant: a separate kernel writes the bf16 "
@@ -103,6 +177,9 @@ def main() -> int:
 
     if args.copy_calibration_mib:
         return copy_calibration(args, torch)
+    if args.workload in gen.GDN_WORKLOADS:
+        B.lib()  # raises if the HIP library is missing
+        return run_gdn(args, gen.GDN_WORKLOADS[args.workload], torch, B, gen)
     if args.workload not in gen.WORKLOADS:
         print(f"unknown workload {args.workload}", file=sys.stderr)
         return 2

@@ -1,5 +1,5 @@
 """Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h,
-include/moe_q4_ablation.h and include/moe_q4_decode.h).
+include/moe_q4_ablation.h, include/moe_q4_decode.h and include/gdn_scan.h).
 
 Argument marshalling only: torch tensors supply device memory and the HIP
 stream, every step of the layer runs in the library's HIP kernels.  There is
@@ -51,6 +51,11 @@ class RouteOutDesc(ctypes.Structure):
                 ("sorted_idx", c_p), ("inv_pos", c_p), ("block_map", c_p), ("n_tiles", c_p)]
 
 
+class GdnScanDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("HK", ctypes.c_int32), ("HV", ctypes.c_int32), ("DK", ctypes.c_int32),
+                ("DV", ctypes.c_int32)]
+
+
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route_block_rows": (ctypes.c_int, []),
@@ -77,6 +82,8 @@ SIGNATURES = {
     "moe_decode_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
                                           ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                           c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
+    # the Gated DeltaNet prefill scan (gdn_scan.h)
+    "gdn_prefill_scan": (ctypes.c_int, [ctypes.POINTER(GdnScanDesc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
 }
 MOE_DECODE_MAX_TOKENS = 16
 
@@ -227,3 +234,13 @@ def moe_decode_forward(desc, x, w_router_pm, router_bias, w_gate_up: Q4Desc, w_d
     _chk("moe_decode_forward", lib().moe_decode_forward(
         ctypes.byref(desc), _ptr(x), _ptr(w_router_pm), _ptr(router_bias), byref(w_gate_up), byref(w_down),
         byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gdn_desc(T, HK, HV, DK, DV) -> GdnScanDesc:
+    return GdnScanDesc(T, HK, HV, DK, DV)
+
+
+def gdn_prefill_scan(desc: GdnScanDesc, q, k, v, alpha, beta, state_in, o, state_out, stream=None):
+    _chk("gdn_prefill_scan", lib().gdn_prefill_scan(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(o),
+        _ptr(state_out), _stream(stream)))

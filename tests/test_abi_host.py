@@ -21,12 +21,12 @@ MIS = 0x10008
 
 def header_functions():
     text = "".join(open(h).read() for h in HEADERS)
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(moe_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+((?:moe|gdn)_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(HEADERS) == 3 and len(names) == 13
+    assert len(HEADERS) == 4 and len(names) == 14
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -228,3 +228,26 @@ def test_decode_entry_points_argument_errors():
     big = B.layer_desc(B.MOE_DECODE_MAX_TOKENS + 1, 256, 128, 16, 4)
     assert call(big, ws_bytes=B.moe_workspace_size(big, 1)) == B.MOE_ERR_UNSUPPORTED_SHAPE
     assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
+
+
+def test_gdn_scan_argument_errors():
+    L = B.lib()
+    d = B.gdn_desc(8, 2, 4, 128, 32)
+    call = lambda desc, q=A, k=A, v=A, al=A, be=A, si=None, o=A, so=A + 0x100: L.gdn_prefill_scan(  # noqa: E731
+        ctypes.byref(desc) if desc is not None else None, q, k, v, al, be, si, o, so, None)
+    assert call(None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, so=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, q=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, be=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, si=A + 0x100) == B.MOE_ERR_INVALID_ARGUMENT  # state_in aliases state_out
+    assert call(B.gdn_desc(-1, 2, 4, 128, 32)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(B.gdn_desc(8, 0, 4, 128, 32)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(B.gdn_desc(8, 2, 4, 96, 32)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(B.gdn_desc(8, 2, 4, 128, 24)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(B.gdn_desc(8, 3, 4, 128, 32)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(d, v=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(d, so=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(d, si=MIS) == B.MOE_ERR_MISALIGNED
+    # no tokens: only the state pointers are needed
+    assert call(B.gdn_desc(0, 2, 4, 128, 32), q=None, k=None, v=None, al=None, be=None, o=None,
+                so=MIS) == B.MOE_ERR_MISALIGNED
