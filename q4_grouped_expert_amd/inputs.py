@@ -222,3 +222,56 @@ def make_gdn(shape: GdnShape, seed: Optional[int] = None) -> GdnInputs:
 
 def gdn_shape(T, HK, HV, DK, DV, seed=7, zero_state=False, name="custom") -> GdnShape:
     return GdnShape(name, T=T, HK=HK, HV=HV, DK=DK, DV=DV, seed=seed, zero_state=zero_state)
+
+
+# ---- Batch-1 GQA decode attention ------------------------------------------
+#
+# Input recipe (independent streams of one seed): the new token's queries
+# q bf16 [HQ, D] ~ N(0, 1); the KV cache in the fixed block layout, blocks of
+# 32 tokens per KV head, K bf16 [nb, HKV, 32, D] (token-major in a block) and
+# V bf16 [nb, HKV, D, 32] (dimension-major in a block), all ~ N(0, 1),
+# including the unused tail of the last block; scale = 1/sqrt(D).  The head
+# layout is the pages': 16 query heads over 2 KV heads; D = 256.
+
+_AQ, _AK, _AV = 201, 202, 203
+GQA_BLOCK = 32
+
+
+@dataclasses.dataclass(frozen=True)
+class GqaShape:
+    name: str
+    L: int
+    HQ: int
+    HKV: int
+    D: int
+    seed: int
+
+
+@dataclasses.dataclass
+class GqaInputs:
+    shape: GqaShape
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    scale: float
+
+
+GQA_WORKLOADS = {
+    "attn_tiny": GqaShape("attn_tiny", L=77, HQ=4, HKV=2, D=128, seed=3001),
+    "attn3840": GqaShape("attn3840", L=3840, HQ=16, HKV=2, D=256, seed=3002),
+    "attn32k": GqaShape("attn32k", L=32768, HQ=16, HKV=2, D=256, seed=3003),
+    "attn128k": GqaShape("attn128k", L=131072, HQ=16, HKV=2, D=256, seed=3004),
+}
+
+
+def make_gqa(shape: GqaShape, seed: Optional[int] = None) -> GqaInputs:
+    sd = shape.seed if seed is None else seed
+    nb = max(1, -(-shape.L // GQA_BLOCK))
+    q = bf16_bits(_rng(sd, _AQ).standard_normal((shape.HQ, shape.D), dtype=np.float32))
+    k = bf16_bits(_rng(sd, _AK).standard_normal((nb, shape.HKV, GQA_BLOCK, shape.D), dtype=np.float32))
+    v = bf16_bits(_rng(sd, _AV).standard_normal((nb, shape.HKV, shape.D, GQA_BLOCK), dtype=np.float32))
+    return GqaInputs(shape, q, k, v, float(1.0 / np.sqrt(shape.D)))
+
+
+def gqa_shape(L, HQ, HKV, D, seed=7, name="custom") -> GqaShape:
+    return GqaShape(name, L=L, HQ=HQ, HKV=HKV, D=D, seed=seed)
