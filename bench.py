@@ -100,6 +100,76 @@ def run_gdn(args, shape, torch, B, gen):
     return 0
 
 
+def run_gqa(args, shape, torch, B, gen):
+    """Batch-1 GQA decode attention (gqa_decode_attention): decode steps/s and,
+    as its roofline, the HBM bytes the step must move (the K and V cache of
+    the context once, q, out) over the step's time."""
+    import numpy as np
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = gen.make_gqa(shape)
+    L, HQ, HKV, D = shape.L, shape.HQ, shape.HKV, shape.D
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)  # noqa: E731
+    q, k, v = u16(inp.q), u16(inp.k), u16(inp.v)
+    desc = B.gqa_desc(L, HQ, HKV, D, inp.scale)
+    nbytes = B.gqa_decode_workspace_size(desc)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((HQ, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.gqa_decode_attention(desc, q, k, v, out, ws, nbytes, stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        B.gqa_decode_attention(desc, q, k, v, out, ws, nbytes, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    hbm = 2 * L * HKV * D * 2 + HQ * D * 2 + HQ * D * 4
+    achieved = hbm / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GQA decode attention steps/s (batch 1)",
+        "value": round(args.steps / elapsed, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: context {L} tokens, {HQ} query heads over {HKV} KV heads, "
+                               f"head dim {D}, KV cache in 32-token blocks", "context": L, "seed": shape.seed},
+        "roofline": {"kernel": "gqa_split_kernel + gqa_combine_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic("gqa_decode", args.workload), "bytes_per_launch": hbm,
+                     "avg_launch_ms": round(step_ms, 4)},
+        "workspace_bytes": nbytes,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.gqa as OA
+
+        threads = min(int(os.environ.get("OMP_NUM_THREADS") or (os.cpu_count() or 1)), os.cpu_count() or 1, HQ)
+        t1 = time.perf_counter()
+        reps = 0
+        while True:
+            OA.decode(L, inp.q, inp.k, inp.v, HKV, inp.scale)
+            reps += 1
+            dt = time.perf_counter() - t1
+            if dt > 2.0 or reps >= 50:
+                break
+        res["cpu_baseline"] = {"value": round(reps / dt, 2), "unit": "steps/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{reps} whole decode steps over the {L}-token context, fp64, {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -148,7 +218,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill4096",
                     help="prefill4096 (default), prefill512, skew2048, long16384, tiny; decode1, decode4, "
-                         "decode16 (decode-shape layer); gdn4096, gdn512, gdn_tiny (Gated DeltaNet prefill scan)")
+                         "decode16 (decode-shape layer); gdn4096, gdn512, gdn_tiny (Gated DeltaNet prefill scan); "
+                         "attn32k, attn128k, attn3840, attn_tiny (batch-1 GQA decode attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused_dequant", "host_sync"],
                     help="fused: the layer as built (default); unfused_dequant: a separate kernel writes the bf16 "
@@ -177,6 +248,9 @@ def main() -> int:
 
     if args.copy_calibration_mib:
         return copy_calibration(args, torch)
+    if args.workload in gen.GQA_WORKLOADS:
+        B.lib()  # raises if the HIP library is missing
+        return run_gqa(args, gen.GQA_WORKLOADS[args.workload], torch, B, gen)
     if args.workload in gen.GDN_WORKLOADS:
         B.lib()  # raises if the HIP library is missing
         return run_gdn(args, gen.GDN_WORKLOADS[args.workload], torch, B, gen)

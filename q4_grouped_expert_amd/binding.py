@@ -1,5 +1,6 @@
 """Thin ctypes binding of libmoeq4.so (the C ABI in include/moe_q4.h,
-include/moe_q4_ablation.h, include/moe_q4_decode.h and include/gdn_scan.h).
+include/moe_q4_ablation.h, include/moe_q4_decode.h, include/gdn_scan.h and
+include/gqa_decode.h).
 
 Argument marshalling only: torch tensors supply device memory and the HIP
 stream, every step of the layer runs in the library's HIP kernels.  There is
@@ -51,6 +52,11 @@ class RouteOutDesc(ctypes.Structure):
                 ("sorted_idx", c_p), ("inv_pos", c_p), ("block_map", c_p), ("n_tiles", c_p)]
 
 
+class GqaDecodeDesc(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("HQ", ctypes.c_int32), ("HKV", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
 class GdnScanDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("HK", ctypes.c_int32), ("HV", ctypes.c_int32), ("DK", ctypes.c_int32),
                 ("DV", ctypes.c_int32)]
@@ -84,7 +90,12 @@ SIGNATURES = {
                                           c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
     # the Gated DeltaNet prefill scan (gdn_scan.h)
     "gdn_prefill_scan": (ctypes.c_int, [ctypes.POINTER(GdnScanDesc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
+    # batch-1 GQA decode attention (gqa_decode.h)
+    "gqa_decode_workspace_size": (ctypes.c_int, [ctypes.POINTER(GqaDecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "gqa_decode_attention": (ctypes.c_int, [ctypes.POINTER(GqaDecodeDesc), c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t,
+                                            c_p]),
 }
+GQA_BLOCK = 32
 MOE_DECODE_MAX_TOKENS = 16
 
 _lib = None
@@ -244,3 +255,18 @@ def gdn_prefill_scan(desc: GdnScanDesc, q, k, v, alpha, beta, state_in, o, state
     _chk("gdn_prefill_scan", lib().gdn_prefill_scan(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(o),
         _ptr(state_out), _stream(stream)))
+
+
+def gqa_desc(L, HQ, HKV, D, scale) -> GqaDecodeDesc:
+    return GqaDecodeDesc(L, HQ, HKV, D, scale)
+
+
+def gqa_decode_workspace_size(desc: GqaDecodeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _chk("gqa_decode_workspace_size", lib().gqa_decode_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def gqa_decode_attention(desc: GqaDecodeDesc, q, k_cache, v_cache, out, ws, ws_bytes, stream=None):
+    _chk("gqa_decode_attention", lib().gqa_decode_attention(
+        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))

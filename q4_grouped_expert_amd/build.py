@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmoeq4.so")
-SOURCES = ["api.hip", "route.hip", "gemm_q4.hip", "dequant.hip", "decode.hip", "combine.hip", "gdn.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm_q4.hip", "dequant.hip", "decode.hip", "combine.hip", "gdn.hip", "gqa.hip"]
 ARCH = os.environ.get("MOE_Q4_ARCH", "gfx950")
 
 

@@ -21,12 +21,12 @@ MIS = 0x10008
 
 def header_functions():
     text = "".join(open(h).read() for h in HEADERS)
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+((?:moe|gdn)_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+((?:moe|gdn|gqa)_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(HEADERS) == 4 and len(names) == 14
+    assert len(HEADERS) == 5 and len(names) == 16
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -251,3 +251,31 @@ def test_gdn_scan_argument_errors():
     # no tokens: only the state pointers are needed
     assert call(B.gdn_desc(0, 2, 4, 128, 32), q=None, k=None, v=None, al=None, be=None, o=None,
                 so=MIS) == B.MOE_ERR_MISALIGNED
+
+
+def test_gqa_decode_argument_errors():
+    L = B.lib()
+    d = B.gqa_desc(100, 16, 2, 256, 0.0625)
+    need = B.gqa_decode_workspace_size(d)
+    assert need > 0
+    n = ctypes.c_size_t(0)
+    assert L.gqa_decode_workspace_size(None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.gqa_decode_workspace_size(ctypes.byref(B.gqa_desc(100, 16, 2, 96, 1.0)),
+                                       ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert L.gqa_decode_workspace_size(ctypes.byref(B.gqa_desc(100, 34, 2, 128, 1.0)),
+                                       ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED_SHAPE  # 17 heads per KV head
+    assert L.gqa_decode_workspace_size(ctypes.byref(B.gqa_desc(100, 15, 2, 128, 1.0)),
+                                       ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert L.gqa_decode_workspace_size(ctypes.byref(B.gqa_desc(-1, 16, 2, 128, 1.0)),
+                                       ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    call = lambda desc, q=A, k=A, v=A, o=A, ws=A, wsb=need: L.gqa_decode_attention(  # noqa: E731
+        ctypes.byref(desc), q, k, v, o, ws, wsb, None)
+    assert call(d, q=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, k=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, ws=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(d, v=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(d, o=MIS) == B.MOE_ERR_MISALIGNED
+    assert call(d, wsb=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # the workspace grows with the context up to the split target
+    sizes = [B.gqa_decode_workspace_size(B.gqa_desc(Lc, 16, 2, 256, 0.0625)) for Lc in (32, 3840, 32768, 131072)]
+    assert sizes[0] < sizes[1] < sizes[2] and sizes[3] <= 2 * sizes[2]
