@@ -532,6 +532,20 @@ def run_decode(args, shape, torch, B, gen):
                      "bytes_per_launch": hbm_bytes, "avg_launch_ms": round(layer_ms, 4)},
         "experts_read": n_ne,
     }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS") or 16))
+        t1 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.layer_forward(inp, nthreads=nthreads)
+            reps += 1
+            dt = time.perf_counter() - t1
+            if dt > 2.0 or reps >= 20:
+                break
+        res["cpu_baseline"] = {"value": round(T * reps / dt, 2), "unit": "tokens/s", "cores": nthreads,
+                               "kind": "oracle", "sample": f"{reps} whole calls of the {T}-token layer, {dt:.1f} s"}
     print(json.dumps(res), flush=True)
     return 0
 
