@@ -99,6 +99,7 @@ UNFUSED = {
     "ragged_T300": gen.custom_shape(300, 512, 256, 32, 4, seed=51),
     "no_shared": gen.custom_shape(90, 256, 192, 16, 4, shared=False, seed=52),
     "H64_I64": gen.custom_shape(50, 64, 64, 8, 2, seed=53),
+    "I512_E8": gen.custom_shape(400, 256, 512, 8, 2, seed=54),
     "prefill512": gen.WORKLOADS["prefill512"],
 }
 

@@ -53,6 +53,9 @@ SMALL = {
     "E40": gen.custom_shape(130, 256, 128, 40, 6, seed=26),
     "no_shared": gen.custom_shape(90, 256, 192, 16, 4, shared=False, seed=27),
     "tall_group": gen.custom_shape(700, 128, 64, 4, 2, seed=28),
+    # reduction 512 with about 100 rows per expert and shared-expert tiles of
+    # 256 and 144 rows
+    "I512_E8": gen.custom_shape(400, 256, 512, 8, 2, seed=36),
     # 16 and 32 quant groups per weight row in both GEMMs (the scale/bias
     # tables' chunk rotation with masks 1 and 3)
     "H1024_I1024": gen.custom_shape(96, 1024, 1024, 16, 4, seed=33),
