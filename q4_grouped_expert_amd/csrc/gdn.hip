@@ -12,7 +12,8 @@
 // one state column per SIMD group and keep it in registers for the whole
 // scan, writing the fp32 state once at the end (aitrends.kr, section
 // "GPU 상주와 메모리 절감").  Here:
-//  * a row is held by 16 lanes (one DPP row), DK/16 fp32 entries each, in
+//  * a row is held by 16 lanes (one DPP row), DK/16 fp32 entries each (in
+//    groups of 4, so that LDS reads of k and q are conflict-free), in
 //    registers from the first token to the last; a wave holds 4 rows and a
 //    workgroup of 4 waves 16 rows of one head, so a 32-head, 128-row layer
 //    runs 256 workgroups, one per CU;
@@ -94,13 +95,18 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
   const int rl = 4 * wave + (lane >> 4);  // row within the workgroup
   const int l16 = lane & 15;
 
-  // this lane's part of the state: row 16*blk + rl of head hv, entries kE*l16 ..
+  // this lane's part of the state: row 16*blk + rl of head hv, entries
+  // 64*(e/4) + 4*l16 + e%4 for e < kE.  Groups of 4 consecutive entries per
+  // lane, 64 apart, so each 16-byte LDS read of k or q by the 16 lanes of a
+  // row covers 256 consecutive bytes: every bank once, no conflict (8
+  // consecutive entries per lane would put two lanes on each bank group).
   float S[kE];
-  const size_t soff = ((size_t)hv * a.DV + kGdnRows * blk + rl) * DK + kE * l16;
+  auto entry = [&](int e) { return 64 * (e / 4) + 4 * l16; };  // first of the 4 entries of group e/4
+  const size_t srow = ((size_t)hv * a.DV + kGdnRows * blk + rl) * DK;
   if (a.state_in) {
 #pragma unroll
     for (int e = 0; e < kE; e += 4) {
-      const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.state_in + soff + e);
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.state_in + srow + entry(e));
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[e + i] = s4[i];
     }
@@ -186,8 +192,8 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
     auto load_step = [&](int s, StepIn& in) {
 #pragma unroll
       for (int e = 0; e < kE; e += 4) {
-        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&kf[b][s][kE * l16 + e]);
-        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qf[b][s][kE * l16 + e]);
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&kf[b][s][entry(e)]);
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qf[b][s][entry(e)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           in.k[e + i] = k4[i];
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
   // the state leaves once, after the last token
 #pragma unroll
   for (int e = 0; e < kE; e += 4)
-    *reinterpret_cast<f32x4*>(a.state_out + soff + e) = f32x4{S[e], S[e + 1], S[e + 2], S[e + 3]};
+    *reinterpret_cast<f32x4*>(a.state_out + srow + entry(e)) = f32x4{S[e], S[e + 1], S[e + 2], S[e + 3]};
 }
 
 inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
