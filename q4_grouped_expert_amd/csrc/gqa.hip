@@ -207,58 +207,91 @@ __global__ __launch_bounds__(kGqaThreads, 2) void gqa_split_kernel(GqaArgs a) {
 }
 
 // out[h][d] = sum over the head's partials of 2^(m_p - M) o_p / the same sum
-// of l_p.  Workgroup (h, slice) takes 64 dims of query head h: the
-// partials' maxima and weights are reduced through LDS, then each of the 4
-// waves streams every fourth partial of its 64 dims with 8 loads in flight,
-// and the 4 wave sums are added in wave order.
+// of l_p.  Workgroup (h, slice) takes 64 dims of query head h.  No load
+// waits for the maximum: every thread first loads its share of the partials'
+// maxima and weights and the first kCombinePre partial outputs of its column
+// (one round trip for up to 4 * kCombinePre partials), then M and the weight
+// sum are reduced across lanes and waves, and each of the 4 waves sums every
+// fourth partial of its 64 dims; longer lists continue with 8 loads in
+// flight.  The 4 wave sums are added in wave order.
 constexpr int kMaxParts = 1024;  // partials per head the combine holds in LDS
 constexpr int kCombineDims = 64;
+constexpr int kCombinePre = 32;  // partial outputs per thread loaded up front
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
 
 __global__ __launch_bounds__(256) void gqa_combine_kernel(GqaArgs a, int D) {
+  constexpr int kPer = kMaxParts / 256;
   __shared__ float f[kMaxParts];
-  __shared__ float red[256];
+  __shared__ float wred[2][4];
   __shared__ float part_o[4][kCombineDims];
   const int nslice = D / kCombineDims;
   const int h = blockIdx.x / nslice, slice = blockIdx.x % nslice;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int G = a.G, g = h / G, hl = h % G;
   const int n = a.wgs;
   const float* pm = a.pm + (size_t)g * n * G + hl;
   const float* pl = a.pl + (size_t)g * n * G + hl;
-  float M = -INFINITY;
-  for (int w = t; w < n; w += 256) M = fmaxf(M, pm[(size_t)w * G]);
-  red[t] = M;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = fmaxf(red[t], red[t + s]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
-  float l = 0.0f;
-  for (int w = t; w < n; w += 256) {
-    const float fw = __builtin_amdgcn_exp2f(pm[(size_t)w * G] - M);
-    f[w] = fw;
-    l += fw * pl[(size_t)w * G];
-  }
-  red[t] = l;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  l = red[0];
   const int dd = t & (kCombineDims - 1), qq = t / kCombineDims;
   const int d = slice * kCombineDims + dd;
   const size_t stride = (size_t)G * D;
   const float* po = a.po + ((size_t)g * n * G + hl) * D + d;
+
+  float mv[kPer], lv[kPer], pre[kCombinePre];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int w = t + 256 * i;
+    mv[i] = w < n ? pm[(size_t)w * G] : -INFINITY;
+    lv[i] = w < n ? pl[(size_t)w * G] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < kCombinePre; ++u) {
+    const int w = qq + 4 * u;
+    pre[u] = w < n ? po[(size_t)w * stride] : 0.0f;
+  }
+
+  float M = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
+  M = wave_max(M);
+  if (lane == 0) wred[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  float l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int w = t + 256 * i;
+    if (w < n) {
+      const float fw = __builtin_amdgcn_exp2f(mv[i] - M);
+      f[w] = fw;
+      l += fw * lv[i];
+    }
+  }
+  l = wave_sum(l);
+  if (lane == 0) wred[1][wave] = l;
+  __syncthreads();
+  l = (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]);
+
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int w = qq;
+#pragma unroll
+  for (int u = 0; u < kCombinePre; ++u) {
+    const int w = qq + 4 * u;
+    if (w < n) o[u % 8] += f[w] * pre[u];
+  }
+  int w = qq + 4 * kCombinePre;
   for (; w + 28 < n; w += 32) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) o[u] += f[w + 4 * u] * po[(size_t)(w + 4 * u) * stride];
   }
-  for (; w < n; w += 4) o[0] += f[w] * po[(size_t)w * stride];
+  for (; w < n; w += 4) o[((w - qq) / 4) % 8] += f[w] * po[(size_t)w * stride];
   part_o[qq][dd] = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
   __syncthreads();
   if (qq == 0)
