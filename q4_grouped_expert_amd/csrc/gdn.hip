@@ -189,6 +189,8 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
       float k[kE], q[kE];
       float v, al, be;
     };
+    static_assert(kChunk == 32, "each lane keeps the outputs of two tokens of a chunk");
+    float keep0 = 0.0f, keep1 = 0.0f;  // outputs of tokens l16 and 16 + l16 of the chunk
     auto load_step = [&](int s, StepIn& in) {
 #pragma unroll
       for (int e = 0; e < kE; e += 4) {
@@ -221,8 +223,13 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
         if (e & 1) o1 = __builtin_fmaf(S[e], in.q[e], o1);
         else o0 = __builtin_fmaf(S[e], in.q[e], o0);
       }
+      // the 16 lanes of the row hold the same sum; lane s % 16 keeps it, so
+      // a chunk's outputs leave through two LDS writes per lane, not one
+      // masked write per token
       const float ov = row16_sum(o0 + o1);
-      if (l16 == 0) ob[s][rl] = ov;
+      const bool mine = l16 == (s & 15);
+      keep0 = mine && s < 16 ? ov : keep0;
+      keep1 = mine && s >= 16 ? ov : keep1;
     };
     // two tokens per iteration, each one's inputs loaded during the previous
     // token, so the output sum of one token overlaps the next one's recall;
@@ -248,6 +255,8 @@ __global__ __launch_bounds__(kGdnThreads, 1) void gdn_scan_kernel(GdnArgs a) {
       }
       if (s < n) step(s, x0);
     }
+    ob[l16][rl] = keep0;
+    ob[16 + l16][rl] = keep1;
     __syncthreads();  // the chunk's outputs are in ob and buffer b is no longer read
     {
       const int s = tid / (kGdnRows / 2), part = tid % (kGdnRows / 2);
