@@ -272,7 +272,9 @@ def main() -> int:
     route = dl.new_route(chunk)
     rdesc = B.route_desc(route)
     h = torch.empty((rows_max, I), dtype=torch.int16, device=dev)
-    y = torch.empty((rows_max, H), dtype=torch.float32, device=dev)
+    # the library's default staging of the down GEMM's rows: bf16 y
+    down_mode, y_dtype = B.MOE_GEMM_DOWN_BF16, B.MOE_DTYPE_BF16
+    y = torch.empty((rows_max, H), dtype=torch.int16, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sgu = dl.s_gate_up.desc if dl.has_shared else None
@@ -320,20 +322,21 @@ def main() -> int:
             mark(1)
             if variant == "fused":
                 B.moe_grouped_gemm_q4(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], dl.gate_up.desc, sgu, rdesc, h,
-                                      stream)
+                                      stream=stream)
                 mark(2)
-                B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h, dl.down.desc, sdn, rdesc, y, stream)
+                B.moe_grouped_gemm_q4(d, down_mode, h, dl.down.desc, sdn, rdesc, y, stream=stream)
                 mark(3)
             else:
                 dequant(dl.gate_up.desc, wgu, sgu, wgu_s if dl.has_shared else None)
                 mark(2)
-                B.moe_grouped_gemm_bf16(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], bgu, bgu_s, rdesc, h, stream)
+                B.moe_grouped_gemm_bf16(d, B.MOE_GEMM_GATE_UP_SWIGLU, dl.x[c0:c1], bgu, bgu_s, rdesc, h,
+                                        stream=stream)
                 mark(3)
                 dequant(dl.down.desc, wdn, sdn, wdn_s if dl.has_shared else None)
                 mark(4)
-                B.moe_grouped_gemm_bf16(d, B.MOE_GEMM_DOWN, h, bdn, bdn_s, rdesc, y, stream)
+                B.moe_grouped_gemm_bf16(d, down_mode, h, bdn, bdn_s, rdesc, y, stream=stream)
                 mark(5)
-            B.moe_combine(d, y, rdesc, out[c0:c1], stream)
+            B.moe_combine(d, y, rdesc, out[c0:c1], y_dtype=y_dtype, stream=stream)
             mark(len(names))
 
     for _ in range(args.warmup):

@@ -85,10 +85,14 @@ typedef struct {
 
 /* Layer shape.  T tokens in this call (one chunk), hidden size H, expert
  * intermediate size I, E routed experts, top_k chosen per token.
+ * group_size: weights per (scale, bias) pair along the reduction axis; the
+ * pages give 64 ("Perplexity Lily 오픈소스 공개", section 5-1), the only
+ * value the kernels take (MOE_ERR_UNSUPPORTED_SHAPE otherwise).
  * norm_topk: 1 = renormalize the weights over the chosen experts.
  * has_shared: 1 = one shared expert with weight 1 for every token. */
 typedef struct {
   int32_t T, H, I, E, top_k;
+  int32_t group_size;
   int32_t norm_topk;
   int32_t has_shared;
 } moe_layer_desc;
@@ -123,61 +127,140 @@ enum moe_gemm_mode {
   MOE_GEMM_GATE_UP_SWIGLU = 0, /* a = x [T][H] bf16 (routed rows gathered through
                                   sorted_idx), w: N=2I (rows [0,I) gate, [I,2I) up),
                                   K=H; c = h bf16 [R(+T)][I] */
-  MOE_GEMM_DOWN = 1            /* a = h bf16 [R(+T)][I]; w: N=H, K=I;
+  MOE_GEMM_DOWN = 1,           /* a = h bf16 [R(+T)][I]; w: N=H, K=I;
                                   c = y fp32 [R(+T)][H] */
+  MOE_GEMM_DOWN_BF16 = 2,      /* as MOE_GEMM_DOWN, c = y rounded to bf16 (RNE) */
+  MOE_GEMM_DOWN_COMBINE = 3    /* as MOE_GEMM_DOWN, but each row's result is
+                                  weighted (topk_w of its (t,k); 1 for a shared
+                                  row) and ADDED into c = out fp32 [T][H] with
+                                  fp32 atomics: the combine fused into the
+                                  epilogue.  c must hold zeros (or values to add
+                                  to) before the call.  The order of the adds is
+                                  not fixed, so results may differ in the last
+                                  bits from run to run. */
+};
+
+/* Element type of the staged expert outputs y handed to moe_combine. */
+enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1
+};
+
+/* How moe_layer_forward_ex hands the down GEMM's rows to the combine. */
+enum moe_combine_mode {
+  MOE_COMBINE_Y_F32 = 0,    /* y fp32 in the workspace, then moe_combine */
+  MOE_COMBINE_Y_BF16 = 1,   /* y bf16 in the workspace, then moe_combine */
+  MOE_COMBINE_FUSED = 2     /* MOE_GEMM_DOWN_COMBINE into out (zeroed by the
+                               gate/up launch); no y, not bitwise reproducible */
 };
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(int status);
 
-/* Rows per GEMM tile used in the block map (host-only, pure). */
+/* Rows per GEMM tile used in the block map (host-only, pure).  The pages
+ * group rows into fixed-height tiles per expert ("Apple silicon용 Lily, Qwen
+ * 추론 최적화", section "GPU 상주와 메모리 절감"); this library's tiles hold
+ * up to this many rows. */
 int moe_route_block_rows(void);
 
 /* Upper bound on block-map entries for `desc`:
- * floor(R/BM) + min(E, R) + (has_shared ? ceil(T/BM) : 0).  Host-only. */
+ * floor(R/BM) + min(E, R) + (has_shared ? ceil(T/BM) : 0).  Host-only, pure.
+ * The GEMM grids are sized from it, so no host round trip is needed to
+ * launch them ("Perplexity Lily 오픈소스 공개", section 5-2). */
 int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 
-/* Workspace bytes needed by moe_route (ws_kind = 0: expert histograms per
- * 64-token group, E * (ceil(T/64) rounded up to 4) int32, 256 fp32
- * router-row norms, a piece-major copy of the router matrix E * H bf16 and
- * the approximate router logits as ns partial sums ns * T * E fp32, ns = 1, 2,
- * 4 or 8 splits of the hidden axis (the most that keep the logit grid at or
- * below 256 workgroups of 64 tokens x 64 experts), each piece 256-byte
- * aligned) or moe_layer_forward (ws_kind = 1; also routing
- * buffers, h and y).  Host-only, pure.  Workspace contents need no
- * initialization and are overwritten. */
-int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes);
+/* Workspace bytes of moe_layer_forward for `desc` (host-only, pure): the
+ * routing scratch, the routing results (used when route_or_null is NULL), h
+ * bf16 [R(+T)][I] and y bf16 [R(+T)][H], each piece 256-byte aligned.  The
+ * same buffer also serves moe_route and moe_grouped_gemm_q4.  The pages keep
+ * temporary activations of a prompt bounded by running it in chunks through
+ * one workspace ("Perplexity Lily 오픈소스 공개", section 5-2; "Apple
+ * silicon용 Lily, Qwen 추론 최적화", section "GPU 상주와 메모리 절감").
+ * Workspace contents need no initialization and are overwritten.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (NULL pointer, bad descriptor),
+ * MOE_ERR_UNSUPPORTED_SHAPE. */
+int moe_layer_workspace_size(const moe_layer_desc* desc, size_t* bytes);
 
-/* Routing, steps histogram -> scan -> scatter -> block map included.
+/* Workspace bytes of moe_layer_forward_ex in `combine_mode` (a
+ * moe_combine_mode): y fp32, y bf16, or no y at all (MOE_COMBINE_FUSED). */
+int moe_layer_workspace_size_ex(const moe_layer_desc* desc, int combine_mode, size_t* bytes);
+
+/* Workspace bytes moe_route alone needs (host-only, pure): expert histograms
+ * per 64-token group, E * (ceil(T/64) rounded up to 4) int32; 256 fp32
+ * router-row norms; a piece-major copy of the router matrix, E * H bf16; the
+ * approximate router logits as ns partial sums, ns * T * E fp32, with ns = 1,
+ * 2, 4 or 8 splits of the hidden axis (the most that keep the logit grid at
+ * or below 256 workgroups of 64 tokens x 64 experts); each piece 256-byte
+ * aligned.  moe_layer_workspace_size is at least this. */
+int moe_route_workspace_size(const moe_layer_desc* desc, size_t* bytes);
+
+/* Routing, steps histogram -> scan -> scatter -> block map included, all on
+ * `stream` with no host round trip: per-token selection of top_k of E
+ * experts, then a histogram of the choices, an exclusive prefix scan into
+ * group offsets, a stable scatter into expert groups and the tile block map
+ * ("Perplexity Lily 오픈소스 공개", sections 4 and 5-2; "Apple silicon용 Lily,
+ * Qwen 추론 최적화", sections "Qwen 구조와 Prefill 경로" and "GPU 상주와
+ * 메모리 절감").
  * x bf16 [T][H], w_router bf16 [E][H], router_bias fp32 [E] or NULL.
  * Writes every field of *out (all required; block_map entries past n_tiles
- * are left unspecified).  ws: moe_workspace_size(.., 0) bytes, required. */
+ * are left unspecified).  ws: at least moe_route_workspace_size bytes.
+ * Errors: MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED_SHAPE,
+ * MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. */
 int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
               const float* router_bias, const moe_route_out* out, void* ws, size_t ws_bytes,
               void* stream);
 
-/* One grouped GEMM over the tiles of route->block_map (see moe_gemm_mode).
+/* One grouped GEMM over the tiles of route->block_map (see moe_gemm_mode),
+ * on 4-bit groupwise-affine weights that are dequantized tile by tile inside
+ * the GEMM and never written out ("Perplexity Lily 오픈소스 공개", section 5-1;
+ * "Apple silicon용 Lily, Qwen 추론 최적화", section "Qwen 구조와 Prefill 경로").
  * w: the E routed experts; w_shared: the shared expert (n_exp = 1), required
- * iff desc->has_shared.  Uses route->sorted_idx, block_map and n_tiles. */
+ * iff desc->has_shared.  Reads route->sorted_idx, block_map and n_tiles
+ * (MOE_GEMM_DOWN_COMBINE also topk_w).  ws, ws_bytes: GEMM scratch; the
+ * kernels of this version need none, so ws may be NULL (any ws_bytes is
+ * accepted).  Errors: MOE_ERR_INVALID_ARGUMENT (NULL pointer, unknown mode),
+ * MOE_ERR_UNSUPPORTED_SHAPE (a weight tensor not matching desc and mode),
+ * MOE_ERR_MISALIGNED, MOE_ERR_HIP. */
 int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a,
                         const moe_q4_tensor* w, const moe_q4_tensor* w_shared,
-                        const moe_route_out* route, void* c, void* stream);
+                        const moe_route_out* route, void* c, void* ws, size_t ws_bytes,
+                        void* stream);
 
-/* out fp32 [T][H] = y[R+t] (if has_shared) + sum_k topk_w[t][k] * y[inv_pos[t*top_k+k]],
- * y fp32 [R(+T)][H] from MOE_GEMM_DOWN. */
-int moe_combine(const moe_layer_desc* desc, const float* y, const moe_route_out* route,
+/* The top-k weighted combine back to token order, fp32:
+ * out[t] = y[R+t] (if has_shared) + sum_k topk_w[t][k] * y[inv_pos[t*top_k+k]],
+ * added in that order.  y [R(+T)][H] from MOE_GEMM_DOWN (y_dtype
+ * MOE_DTYPE_F32) or MOE_GEMM_DOWN_BF16 (MOE_DTYPE_BF16).  The pages' layer
+ * sums the chosen experts' outputs with the router weights plus the shared
+ * expert's ("Apple silicon용 Lily, Qwen 추론 최적화", section "Qwen 구조와
+ * Prefill 경로").  Errors: MOE_ERR_INVALID_ARGUMENT (NULL pointer, unknown
+ * y_dtype), MOE_ERR_MISALIGNED, MOE_ERR_HIP. */
+int moe_combine(const moe_layer_desc* desc, const void* y, int y_dtype, const moe_route_out* route,
                 float* out, void* stream);
 
 /* The whole layer for one chunk of T tokens: moe_route, the two grouped GEMMs
- * and moe_combine, all on `stream`.  route_or_null: if non-NULL, routing
- * results are written there; otherwise they live in the workspace.
- * ws: moe_workspace_size(.., 1) bytes. */
+ * and the combine, all on `stream`, in the default combine mode
+ * (MOE_COMBINE_Y_BF16: deterministic).  Long prompts call it once per bounded
+ * chunk with the same workspace ("Perplexity Lily 오픈소스 공개", section 5-2).
+ * route_or_null: if non-NULL, routing results are written there; otherwise
+ * they live in the workspace.  ws: moe_layer_workspace_size bytes.
+ * Errors: as moe_route and moe_grouped_gemm_q4. */
 int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
                       const float* router_bias, const moe_q4_tensor* w_gate_up,
                       const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                       const moe_q4_tensor* shared_down, float* out,
                       const moe_route_out* route_or_null, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* moe_layer_forward in an explicit moe_combine_mode; ws:
+ * moe_layer_workspace_size_ex(desc, combine_mode) bytes.  MOE_COMBINE_FUSED
+ * zeroes `out` in the gate/up launch and adds into it in the down launch, so
+ * its outputs may differ in the last bits between runs. */
+int moe_layer_forward_ex(const moe_layer_desc* desc, int combine_mode, const uint16_t* x,
+                         const uint16_t* w_router, const float* router_bias,
+                         const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
+                         const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down,
+                         float* out, const moe_route_out* route_or_null, void* ws, size_t ws_bytes,
+                         void* stream);
 
 #ifdef __cplusplus
 }

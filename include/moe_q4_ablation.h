@@ -45,16 +45,19 @@ int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null
 
 /* moe_grouped_gemm_q4 with bf16 weights read from memory instead of 4-bit
  * codes dequantized in the kernel: same modes, tiles, row order and
- * epilogues.  w: the E routed experts; w_shared: the shared expert
- * (n_exp = 1), required iff desc->has_shared. */
+ * epilogues (ws, ws_bytes as there: unused, may be NULL).  w: the E routed
+ * experts; w_shared: the shared expert (n_exp = 1), required iff
+ * desc->has_shared. */
 int moe_grouped_gemm_bf16(const moe_layer_desc* desc, int mode, const void* a, const moe_bf16_tensor* w,
-                          const moe_bf16_tensor* w_shared, const moe_route_out* route, void* c, void* stream);
+                          const moe_bf16_tensor* w_shared, const moe_route_out* route, void* c, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* moe_layer_forward with a host round trip after routing: the routing
  * kernels run, then the host copies n_tiles back, waits for the stream and
  * launches the GEMMs with exactly n_tiles tiles instead of the host-known
  * bound.  This entry point SYNCHRONIZES `stream` once and therefore cannot
- * be captured into a HIP graph.  Arguments as for moe_layer_forward. */
+ * be captured into a HIP graph.  Arguments, workspace and combine mode as
+ * for moe_layer_forward. */
 int moe_layer_forward_host_sync(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
                                 const float* router_bias, const moe_q4_tensor* w_gate_up,
                                 const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,

@@ -37,8 +37,9 @@ int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_rout
  * (counts, offsets, stable sorted_idx / inv_pos, a block map with one tile per
  * expert with rows and then the shared expert's), gate/up + SwiGLU, down and
  * the combine, all on `stream`.  w_router_pm: from
- * moe_decode_router_prepare.  Other arguments and the workspace
- * (moe_workspace_size(desc, 1) bytes) as for moe_layer_forward. */
+ * moe_decode_router_prepare.  Other arguments, the workspace
+ * (moe_layer_workspace_size bytes) and the combine mode as for
+ * moe_layer_forward. */
 int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
                        const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
                        const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,

@@ -26,6 +26,14 @@ MOE_ERR_MISALIGNED = 4
 MOE_ERR_HIP = 5
 MOE_GEMM_GATE_UP_SWIGLU = 0
 MOE_GEMM_DOWN = 1
+MOE_GEMM_DOWN_BF16 = 2
+MOE_GEMM_DOWN_COMBINE = 3
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_COMBINE_Y_F32 = 0
+MOE_COMBINE_Y_BF16 = 1
+MOE_COMBINE_FUSED = 2
+MOE_GROUP_SIZE = 64
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 16
 
@@ -44,7 +52,8 @@ class Bf16Desc(ctypes.Structure):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("has_shared", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
+                ("has_shared", ctypes.c_int32)]
 
 
 class RouteOutDesc(ctypes.Structure):
@@ -66,19 +75,29 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route_block_rows": (ctypes.c_int, []),
     "moe_route_max_tiles": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_int32)]),
-    "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_layer_workspace_size": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_layer_workspace_size_ex": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_route_workspace_size": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(RouteOutDesc),
                                  c_p, ctypes.c_size_t, c_p]),
     "moe_grouped_gemm_q4": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, c_p, ctypes.POINTER(Q4Desc),
-                                           ctypes.POINTER(Q4Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p]),
-    "moe_combine": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, ctypes.POINTER(RouteOutDesc), c_p, c_p]),
+                                           ctypes.POINTER(Q4Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p,
+                                           ctypes.c_size_t, c_p]),
+    "moe_combine": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, ctypes.c_int, ctypes.POINTER(RouteOutDesc), c_p,
+                                   c_p]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
                                          ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                          c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
+    "moe_layer_forward_ex": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, c_p, c_p, c_p,
+                                            ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
+                                            ctypes.POINTER(Q4Desc), c_p, ctypes.POINTER(RouteOutDesc), c_p,
+                                            ctypes.c_size_t, c_p]),
     # the unfused-dequant and host-round-trip variants (moe_q4_ablation.h)
     "moe_dequant_q4_to_bf16": (ctypes.c_int, [ctypes.POINTER(Q4Desc), c_p, c_p, c_p]),
     "moe_grouped_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int, c_p, ctypes.POINTER(Bf16Desc),
-                                             ctypes.POINTER(Bf16Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p]),
+                                             ctypes.POINTER(Bf16Desc), ctypes.POINTER(RouteOutDesc), c_p, c_p,
+                                             ctypes.c_size_t, c_p]),
     "moe_layer_forward_host_sync": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
                                                    ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                                    ctypes.POINTER(Q4Desc), c_p, ctypes.POINTER(RouteOutDesc), c_p,
@@ -149,8 +168,8 @@ def _chk(fn, rc):
 
 # ------------------------------------------------------------------ descriptors
 
-def layer_desc(T, H, I, E, top_k, norm_topk=1, has_shared=1) -> LayerDesc:
-    return LayerDesc(T, H, I, E, top_k, int(norm_topk), int(has_shared))
+def layer_desc(T, H, I, E, top_k, norm_topk=1, has_shared=1, group_size=MOE_GROUP_SIZE) -> LayerDesc:
+    return LayerDesc(T, H, I, E, top_k, int(group_size), int(norm_topk), int(has_shared))
 
 
 def q4_desc(codes, scales, biases, n_exp, N, K) -> Q4Desc:
@@ -174,10 +193,22 @@ def moe_route_max_tiles(desc: LayerDesc) -> int:
     return n.value
 
 
-def moe_workspace_size(desc: LayerDesc, kind: int) -> int:
+def _size(fn, *args) -> int:
     n = ctypes.c_size_t()
-    _chk("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(desc), kind, ctypes.byref(n)))
+    _chk(fn, getattr(lib(), fn)(*args, ctypes.byref(n)))
     return n.value
+
+
+def moe_layer_workspace_size(desc: LayerDesc) -> int:
+    return _size("moe_layer_workspace_size", ctypes.byref(desc))
+
+
+def moe_layer_workspace_size_ex(desc: LayerDesc, combine_mode: int) -> int:
+    return _size("moe_layer_workspace_size_ex", ctypes.byref(desc), combine_mode)
+
+
+def moe_route_workspace_size(desc: LayerDesc) -> int:
+    return _size("moe_route_workspace_size", ctypes.byref(desc))
 
 
 def moe_route(desc, x, w_router, router_bias, route: RouteOutDesc, ws, ws_bytes, stream=None):
@@ -186,14 +217,15 @@ def moe_route(desc, x, w_router, router_bias, route: RouteOutDesc, ws, ws_bytes,
 
 
 def moe_grouped_gemm_q4(desc, mode, a, w: Q4Desc, w_shared: Optional[Q4Desc], route: RouteOutDesc, c,
-                        stream=None):
+                        ws=None, ws_bytes=0, stream=None):
     _chk("moe_grouped_gemm_q4", lib().moe_grouped_gemm_q4(
         ctypes.byref(desc), mode, _ptr(a), ctypes.byref(w),
-        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _stream(stream)))
+        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _ptr(ws), ws_bytes,
+        _stream(stream)))
 
 
-def moe_combine(desc, y, route: RouteOutDesc, out, stream=None):
-    _chk("moe_combine", lib().moe_combine(ctypes.byref(desc), _ptr(y), ctypes.byref(route), _ptr(out),
+def moe_combine(desc, y, route: RouteOutDesc, out, y_dtype=MOE_DTYPE_F32, stream=None):
+    _chk("moe_combine", lib().moe_combine(ctypes.byref(desc), _ptr(y), y_dtype, ctypes.byref(route), _ptr(out),
                                           _stream(stream)))
 
 
@@ -204,6 +236,16 @@ def moe_layer_forward(desc, x, w_router, router_bias, w_gate_up: Q4Desc, w_down:
     _chk("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), byref(w_gate_up), byref(w_down),
         byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def moe_layer_forward_ex(desc, combine_mode, x, w_router, router_bias, w_gate_up: Q4Desc, w_down: Q4Desc,
+                         shared_gate_up: Optional[Q4Desc], shared_down: Optional[Q4Desc], out,
+                         route: Optional[RouteOutDesc], ws, ws_bytes, stream=None):
+    byref = lambda d: ctypes.byref(d) if d is not None else None  # noqa: E731
+    _chk("moe_layer_forward_ex", lib().moe_layer_forward_ex(
+        ctypes.byref(desc), combine_mode, _ptr(x), _ptr(w_router), _ptr(router_bias), byref(w_gate_up),
+        byref(w_down), byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes,
         _stream(stream)))
 
 
@@ -227,10 +269,11 @@ def moe_dequant_q4_to_bf16(w: Q4Desc, counts, out, stream=None):
 
 
 def moe_grouped_gemm_bf16(desc, mode, a, w: Bf16Desc, w_shared: Optional[Bf16Desc], route: RouteOutDesc, c,
-                          stream=None):
+                          ws=None, ws_bytes=0, stream=None):
     _chk("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
         ctypes.byref(desc), mode, _ptr(a), ctypes.byref(w),
-        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _stream(stream)))
+        ctypes.byref(w_shared) if w_shared is not None else None, ctypes.byref(route), _ptr(c), _ptr(ws), ws_bytes,
+        _stream(stream)))
 
 
 def moe_decode_router_prepare(desc, w_router, w_router_pm, stream=None):

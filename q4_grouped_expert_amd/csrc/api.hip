@@ -26,6 +26,8 @@ int check_desc(const moe_layer_desc* d) {
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->top_k <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if ((d->norm_topk != 0 && d->norm_topk != 1) || (d->has_shared != 0 && d->has_shared != 1))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (d->group_size <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (d->group_size != MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->H % MOE_GROUP_SIZE || d->I % MOE_GROUP_SIZE) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->H > MOE_MAX_REDUCTION || d->I > MOE_MAX_REDUCTION) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->E) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -50,7 +52,10 @@ struct Layout {
   size_t h, y, total;
 };
 
-Layout layout_of(const moe_layer_desc* d) {
+// The default combine mode of moe_layer_forward and its variants.
+constexpr int kDefaultCombine = MOE_COMBINE_Y_BF16;
+
+Layout layout_of(const moe_layer_desc* d, int combine_mode = kDefaultCombine) {
   const size_t R = (size_t)d->T * d->top_k;
   const size_t rows = R + (d->has_shared ? (size_t)d->T : 0);
   Layout L;
@@ -71,7 +76,8 @@ Layout layout_of(const moe_layer_desc* d) {
   L.ntiles = take(4);
   L.route_end = o;
   L.h = take(rows * (size_t)d->I * 2);
-  L.y = take(rows * (size_t)d->H * 4);
+  const size_t y_elem = combine_mode == MOE_COMBINE_Y_F32 ? 4 : combine_mode == MOE_COMBINE_Y_BF16 ? 2 : 0;
+  L.y = take(rows * (size_t)d->H * y_elem);
   L.total = o;
   return L;
 }
@@ -120,10 +126,16 @@ struct GemmWeights {
   const uint16_t* bfs = nullptr;
 };
 
+// The down GEMM's epilogue for a moe_gemm_mode (gate/up: unused).
+int out_mode_of(int mode) {
+  return mode == MOE_GEMM_DOWN_BF16 ? kOutBf16 : mode == MOE_GEMM_DOWN_COMBINE ? kOutCombine : kOutF32;
+}
+
 // tiles > 0: launch exactly that many tiles (known on the host) instead of
-// the bound max_tiles_of(d).
+// the bound max_tiles_of(d).  zero_out: a gate/up launch also clears T*H
+// floats there (the fused combine's output).
 int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights& w, const moe_route_out* r, void* c,
-            hipStream_t s, int tiles = 0, bool decode = false) {
+            hipStream_t s, int tiles = 0, bool decode = false, float* zero_out = nullptr) {
   GemmArgs g;
   g.a = reinterpret_cast<const uint16_t*>(a);
   g.codes = w.q ? w.q->codes : nullptr;
@@ -138,6 +150,10 @@ int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights&
   g.block_map = r->block_map;
   g.n_tiles = r->n_tiles;
   g.c = c;
+  g.out_mode = out_mode_of(mode);
+  g.topk_w = r->topk_w;
+  g.zero_out = zero_out;
+  g.zero_n = zero_out ? (size_t)d->T * d->H : 0;
   g.T = d->T;
   g.E = d->E;
   g.topk = d->top_k;
@@ -154,9 +170,11 @@ int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights&
   return hip_status(decode ? launch_decode_gemv(g, false, s) : launch_gemm_down(g, s));
 }
 
-int do_combine(const moe_layer_desc* d, const float* y, const moe_route_out* r, float* out, hipStream_t s) {
+int do_combine(const moe_layer_desc* d, const void* y, int y_dtype, const moe_route_out* r, float* out,
+               hipStream_t s) {
   CombineArgs c;
   c.y = y;
+  c.y_bf16 = y_dtype == MOE_DTYPE_BF16;
   c.topk_w = r->topk_w;
   c.inv_pos = r->inv_pos;
   c.out = out;
@@ -184,9 +202,12 @@ int check_bf16(const moe_bf16_tensor* t, int n_exp, int N, int K) {
 int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                   const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                   const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null, void* ws,
-                  size_t ws_bytes, void* stream, bool host_sync, const float* decode_wf = nullptr) {
+                  size_t ws_bytes, void* stream, bool host_sync, const float* decode_wf = nullptr,
+                  int combine_mode = kDefaultCombine) {
   int rc = check_desc(desc);
   if (rc) return rc;
+  if (combine_mode != MOE_COMBINE_Y_F32 && combine_mode != MOE_COMBINE_Y_BF16 && combine_mode != MOE_COMBINE_FUSED)
+    return MOE_ERR_INVALID_ARGUMENT;
   const bool decode = decode_wf != nullptr;
   if (decode && desc->T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (desc->T == 0) return MOE_OK;
@@ -203,7 +224,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   if (misaligned(x) || misaligned(w_router) || misaligned(out) || misaligned(ws) ||
       (router_bias && misaligned(router_bias)))
     return MOE_ERR_MISALIGNED;
-  const Layout L = layout_of(desc);
+  const Layout L = layout_of(desc, combine_mode);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   char* base = reinterpret_cast<char*>(ws);
@@ -222,7 +243,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
     r.n_tiles = reinterpret_cast<int32_t*>(base + L.ntiles);
   }
   void* h = base + L.h;
-  float* y = reinterpret_cast<float*>(base + L.y);
+  void* y = base + L.y;
   if (decode) {
     DecodeRouteArgs a;
     a.x = x;
@@ -256,9 +277,15 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   // decode: the split-reduction GEMV for a single token, the tiled GEMM from
   // two tokens on (measured faster there on MI355X)
   const bool gemv = decode && desc->T <= kDecodeGemvMaxTokens;
+  if (combine_mode == MOE_COMBINE_FUSED) {
+    // gate/up clears out, down adds every weighted row into it
+    if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out))) return rc;
+    return do_gemm(desc, MOE_GEMM_DOWN_COMBINE, h, dn, &r, out, s, tiles, gemv);
+  }
+  const bool bf = combine_mode == MOE_COMBINE_Y_BF16;
   if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv))) return rc;
-  if ((rc = do_gemm(desc, MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv))) return rc;
-  return do_combine(desc, y, &r, out, s);
+  if ((rc = do_gemm(desc, bf ? MOE_GEMM_DOWN_BF16 : MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv))) return rc;
+  return do_combine(desc, y, bf ? MOE_DTYPE_BF16 : MOE_DTYPE_F32, &r, out, s);
 }
 
 }  // namespace
@@ -287,11 +314,29 @@ int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles) {
   return MOE_OK;
 }
 
-int moe_workspace_size(const moe_layer_desc* desc, int ws_kind, size_t* bytes) {
+int moe_layer_workspace_size(const moe_layer_desc* desc, size_t* bytes) {
   int rc = check_desc(desc);
   if (rc) return rc;
-  if (!bytes || (ws_kind != 0 && ws_kind != 1)) return MOE_ERR_INVALID_ARGUMENT;
-  *bytes = ws_kind == 0 ? route_workspace_bytes(desc->T, desc->H, desc->E) : layout_of(desc).total;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = layout_of(desc).total;
+  return MOE_OK;
+}
+
+int moe_layer_workspace_size_ex(const moe_layer_desc* desc, int combine_mode, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (combine_mode != MOE_COMBINE_Y_F32 && combine_mode != MOE_COMBINE_Y_BF16 && combine_mode != MOE_COMBINE_FUSED)
+    return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = layout_of(desc, combine_mode).total;
+  return MOE_OK;
+}
+
+int moe_route_workspace_size(const moe_layer_desc* desc, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = route_workspace_bytes(desc->T, desc->H, desc->E);
   return MOE_OK;
 }
 
@@ -309,13 +354,17 @@ int moe_route(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_r
 }
 
 int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, const moe_q4_tensor* w,
-                        const moe_q4_tensor* w_shared, const moe_route_out* route, void* c, void* stream) {
+                        const moe_q4_tensor* w_shared, const moe_route_out* route, void* c, void* ws,
+                        size_t ws_bytes, void* stream) {
+  (void)ws;  // no GEMM scratch in this version
+  (void)ws_bytes;
   int rc = check_desc(desc);
   if (rc) return rc;
-  if (mode != MOE_GEMM_GATE_UP_SWIGLU && mode != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
+  if (mode < MOE_GEMM_GATE_UP_SWIGLU || mode > MOE_GEMM_DOWN_COMBINE) return MOE_ERR_INVALID_ARGUMENT;
   if (desc->T == 0) return MOE_OK;
   if (!a || !c || !route || !route->sorted_idx || !route->block_map || !route->n_tiles)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (mode == MOE_GEMM_DOWN_COMBINE && !route->topk_w) return MOE_ERR_INVALID_ARGUMENT;
   const int N = mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 * desc->I : desc->H;
   const int K = mode == MOE_GEMM_GATE_UP_SWIGLU ? desc->H : desc->I;
   if ((rc = check_q4(w, desc->E, N, K))) return rc;
@@ -325,7 +374,7 @@ int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, con
     w_shared = nullptr;
   }
   if (misaligned(a) || misaligned(c) || misaligned(route->sorted_idx) || misaligned(route->block_map) ||
-      misaligned(route->n_tiles))
+      misaligned(route->n_tiles) || (mode == MOE_GEMM_DOWN_COMBINE && misaligned(route->topk_w)))
     return MOE_ERR_MISALIGNED;
   GemmWeights gw;
   gw.q = w;
@@ -333,14 +382,16 @@ int moe_grouped_gemm_q4(const moe_layer_desc* desc, int mode, const void* a, con
   return do_gemm(desc, mode, a, gw, route, c, reinterpret_cast<hipStream_t>(stream));
 }
 
-int moe_combine(const moe_layer_desc* desc, const float* y, const moe_route_out* route, float* out, void* stream) {
+int moe_combine(const moe_layer_desc* desc, const void* y, int y_dtype, const moe_route_out* route, float* out,
+                void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (desc->T == 0) return MOE_OK;
   if (!y || !out || !route || !route->topk_w || !route->inv_pos) return MOE_ERR_INVALID_ARGUMENT;
   if (misaligned(y) || misaligned(out) || misaligned(route->topk_w) || misaligned(route->inv_pos))
     return MOE_ERR_MISALIGNED;
-  return do_combine(desc, y, route, out, reinterpret_cast<hipStream_t>(stream));
+  return do_combine(desc, y, y_dtype, route, out, reinterpret_cast<hipStream_t>(stream));
 }
 
 int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
@@ -349,6 +400,14 @@ int moe_layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint1
                       const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
   return layer_forward(desc, x, w_router, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
                        route_or_null, ws, ws_bytes, stream, false);
+}
+
+int moe_layer_forward_ex(const moe_layer_desc* desc, int combine_mode, const uint16_t* x, const uint16_t* w_router,
+                         const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
+                         const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
+                         const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward(desc, x, w_router, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
+                       route_or_null, ws, ws_bytes, stream, false, nullptr, combine_mode);
 }
 
 int moe_layer_forward_host_sync(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router,
@@ -404,15 +463,19 @@ int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null
 }
 
 int moe_grouped_gemm_bf16(const moe_layer_desc* desc, int mode, const void* a, const moe_bf16_tensor* w,
-                          const moe_bf16_tensor* w_shared, const moe_route_out* route, void* c, void* stream) {
+                          const moe_bf16_tensor* w_shared, const moe_route_out* route, void* c, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
   int rc = check_desc(desc);
   if (rc) return rc;
-  if (mode != MOE_GEMM_GATE_UP_SWIGLU && mode != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
+  if (mode < MOE_GEMM_GATE_UP_SWIGLU || mode > MOE_GEMM_DOWN_COMBINE) return MOE_ERR_INVALID_ARGUMENT;
   if (desc->T == 0) return MOE_OK;
   if (!a || !c || !route || !route->sorted_idx || !route->block_map || !route->n_tiles)
     return MOE_ERR_INVALID_ARGUMENT;
   const int N = mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 * desc->I : desc->H;
   const int K = mode == MOE_GEMM_GATE_UP_SWIGLU ? desc->H : desc->I;
+  if (mode == MOE_GEMM_DOWN_COMBINE && !route->topk_w) return MOE_ERR_INVALID_ARGUMENT;
   if ((rc = check_bf16(w, desc->E, N, K))) return rc;
   if (desc->has_shared) {
     if ((rc = check_bf16(w_shared, 1, N, K))) return rc;

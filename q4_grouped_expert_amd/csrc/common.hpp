@@ -67,11 +67,19 @@ struct GemmArgs {
   const int32_t* block_map;
   const int32_t* n_tiles;
   void* c;                  // output
+  int out_mode;             // down: kOutF32, kOutBf16 or kOutCombine
+  const float* topk_w;      // kOutCombine: weight of each (t, k)
+  float* zero_out;          // gate/up: if set, the launch zeroes zero_n floats here
+  size_t zero_n;
   int T, E, topk, R;
   int N, Kdim;              // weight matrix [N][Kdim]
   int I;                    // gate/up: intermediate size (h width)
   int max_tiles;
 };
+// Down-GEMM epilogues: y fp32, y bf16, or the weighted rows added into out.
+constexpr int kOutF32 = 0;
+constexpr int kOutBf16 = 1;
+constexpr int kOutCombine = 2;
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream);
 
@@ -102,7 +110,8 @@ hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream);
 hipError_t launch_decode_gemv(const GemmArgs& g, bool gate_up, hipStream_t stream);
 
 struct CombineArgs {
-  const float* y;
+  const void* y;            // fp32 or bf16 [R(+T)][H]
+  int y_bf16;
   const float* topk_w;
   const int32_t* inv_pos;
   float* out;

@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) f32x4 part[kDecWaves][2][64];
   const int nslice = kGateUp ? g.I / 16 : g.N / 32;
   const int tile = blockIdx.x / nslice, sl = blockIdx.x - tile * nslice;
+  if (kGateUp) zero_share(g);
   // the block-map entry is read together with n_tiles (entries past n_tiles
   // lie inside the map and are not used)
   const int4 bm = *reinterpret_cast<const int4*>(g.block_map + 4 * tile);
@@ -421,9 +422,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(GemmArgs g) {
     uint16_t* h = reinterpret_cast<uint16_t*>(g.c);
     *reinterpret_cast<u32x2*>(&h[(size_t)r * g.I + 16 * sl + 4 * lg]) = u32x2{hv[0], hv[1]};
   } else {
-    float* y = reinterpret_cast<float*>(g.c);
-    *reinterpret_cast<f32x4*>(&y[(size_t)r * g.N + 32 * sl + 4 * lg]) = s0;
-    *reinterpret_cast<f32x4*>(&y[(size_t)r * g.N + 32 * sl + 16 + 4 * lg]) = s1;
+    const DownRow dr = down_row(g, r);
+    store_down4(g, dr, 32 * sl + 4 * lg, s0);
+    store_down4(g, dr, 32 * sl + 16 + 4 * lg, s1);
   }
 }
 

@@ -51,5 +51,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// A gate/up launch of the fused-combine layer also clears `out` (read by the
+// down launch that follows on the stream): block b of the grid clears its
+// share, 16 bytes per thread and step.
+__device__ __forceinline__ void zero_share(const GemmArgs& g) {
+  if (!g.zero_out) return;
+  const size_t per = ((g.zero_n + gridDim.x - 1) / gridDim.x + 3) & ~size_t(3);
+  const size_t z0 = (size_t)blockIdx.x * per;
+  const size_t z1 = z0 + per < g.zero_n ? z0 + per : g.zero_n;
+  for (size_t i = z0 + 4 * threadIdx.x; i < z1; i += 4 * blockDim.x)
+    *reinterpret_cast<f32x4*>(g.zero_out + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Down-GEMM output row p (grouped order): where its elements go in g.c and,
+// for the fused combine, the weight it is added with.  Routed row p holds
+// (t, k) = sorted_idx[p]; shared-expert rows p >= R hold token p - R with
+// weight 1.
+struct DownRow {
+  size_t base;  // element offset of the row's first column in g.c
+  float w;
+};
+__device__ __forceinline__ DownRow down_row(const GemmArgs& g, int p) {
+  if (g.out_mode != kOutCombine) return DownRow{(size_t)p * g.N, 1.0f};
+  if (p < g.R) {
+    const int s = g.sorted_idx[p];
+    return DownRow{(size_t)(s / g.topk) * g.N, g.topk_w[s]};
+  }
+  return DownRow{(size_t)(p - g.R) * g.N, 1.0f};
+}
+
+// Four consecutive output columns col..col+3 of a down row: stored as fp32
+// or bf16 (RNE) y, or weighted and added into out with fp32 atomics.
+__device__ __forceinline__ void store_down4(const GemmArgs& g, const DownRow& r, int col, const f32x4& v) {
+  if (g.out_mode == kOutBf16) {
+    uint16_t* y = reinterpret_cast<uint16_t*>(g.c) + r.base + col;
+    *reinterpret_cast<u32x2*>(y) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else if (g.out_mode == kOutCombine) {
+    float* o = reinterpret_cast<float*>(g.c) + r.base + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, r.w * v[i]);
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + r.base + col) = v;
+  }
+}
+
 }  // namespace gemm
 }  // namespace moeq4

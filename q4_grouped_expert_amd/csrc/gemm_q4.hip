@@ -216,20 +216,18 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, 
       }
     }
   } else {
-    float* y = reinterpret_cast<float*>(g.c);
 #pragma unroll
     for (int m = 0; m < MSUB; ++m) {
       const int r = m * 16 + r_in;
       if (r < t.nrows) {
+        const DownRow dr = down_row(g, t.row0 + r);
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-          if (t.jval[j])
-            *reinterpret_cast<f32x4*>(&y[(size_t)(t.row0 + r) * g.N + t.ocol[j] - ln + 4 * lg]) = acc[m][j];
+          if (t.jval[j]) store_down4(g, dr, t.ocol[j] - ln + 4 * lg, acc[m][j]);
       }
     }
   }
 }
-
 
 template <bool kGateUp, bool kBf16W, int MSUB>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, const LdsQ& L,
@@ -533,6 +531,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   const int rem = b % (kXcds * nN);
   const int nb = rem / kXcds;
   const int lin = grp * kXcds + rem % kXcds;  // tile rank, largest first
+  if (kGateUp) zero_share(g);
   const int n_tiles = *g.n_tiles;
   if (lin >= n_tiles) return;
   const int tile = n_tiles - 1 - lin;

@@ -40,7 +40,8 @@ class DeviceLayer:
     """One MoE layer's weights in HBM plus a reusable workspace for chunks of
     at most ``chunk`` tokens."""
 
-    def __init__(self, inp: LayerInputs, device="cuda", chunk: Optional[int] = None, norm_topk: int = 1):
+    def __init__(self, inp: LayerInputs, device="cuda", chunk: Optional[int] = None, norm_topk: int = 1,
+                 combine_mode: Optional[int] = None):
         s = inp.shape
         self.shape = s
         self.device = device
@@ -54,11 +55,14 @@ class DeviceLayer:
         self.s_gate_up = DeviceQ4(inp.shared_gate_up, device) if self.has_shared else None
         self.s_down = DeviceQ4(inp.shared_down, device) if self.has_shared else None
         self.chunk = chunk or (s.chunk or s.T)
+        # None: moe_layer_forward's default; else moe_layer_forward_ex in that mode
+        self.combine_mode = combine_mode
         d = self.desc(self.chunk)
-        self.ws_bytes = B.moe_workspace_size(d, 1)
+        self.ws_bytes = (B.moe_layer_workspace_size(d) if combine_mode is None
+                         else B.moe_layer_workspace_size_ex(d, combine_mode))
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.max_tiles = B.moe_route_max_tiles(d)
-        self.route_ws_bytes = B.moe_workspace_size(d, 0)
+        self.route_ws_bytes = B.moe_route_workspace_size(d)
         self.route_ws = torch.empty(max(self.route_ws_bytes, 256), dtype=torch.uint8, device=device)
 
     def desc(self, T: int) -> B.LayerDesc:
@@ -72,10 +76,15 @@ class DeviceLayer:
         T = x.shape[0]
         assert T <= self.chunk
         rd = B.route_desc(route) if route is not None else None
-        B.moe_layer_forward(self.desc(T), x, self.w_router, self.router_bias, self.gate_up.desc, self.down.desc,
-                            self.s_gate_up.desc if self.has_shared else None,
-                            self.s_down.desc if self.has_shared else None, out, rd, self.ws, self.ws_bytes,
-                            stream)
+        sgu = self.s_gate_up.desc if self.has_shared else None
+        sdn = self.s_down.desc if self.has_shared else None
+        if self.combine_mode is None:
+            B.moe_layer_forward(self.desc(T), x, self.w_router, self.router_bias, self.gate_up.desc, self.down.desc,
+                                sgu, sdn, out, rd, self.ws, self.ws_bytes, stream)
+        else:
+            B.moe_layer_forward_ex(self.desc(T), self.combine_mode, x, self.w_router, self.router_bias,
+                                   self.gate_up.desc, self.down.desc, sgu, sdn, out, rd, self.ws, self.ws_bytes,
+                                   stream)
 
     def decode_router(self) -> torch.Tensor:
         """The fp32 piece-major router copy the decode path reads (made once)."""

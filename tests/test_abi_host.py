@@ -26,7 +26,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(HEADERS) == 5 and len(names) == 16
+    assert len(HEADERS) == 5 and len(names) == 19
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -51,7 +51,7 @@ def full_call(desc, x=A, wr=A, rb=None, gu=None, dn=None, sgu=None, sdn=None, ou
     sgu = sgu or q4(1, 2 * d.I, d.H)
     sdn = sdn or q4(1, d.H, d.I)
     if ws_bytes is None:
-        ws_bytes = B.moe_workspace_size(d, 1) if B.lib() and d.H > 0 and d.E > 0 else 0
+        ws_bytes = B.moe_layer_workspace_size(d) if B.lib() and d.H > 0 and d.E > 0 else 0
     return B.lib().moe_layer_forward(ctypes.byref(d), x, wr, rb, ctypes.byref(gu), ctypes.byref(dn),
                                      ctypes.byref(sgu), ctypes.byref(sdn), out,
                                      ctypes.byref(route) if route is not None else None, ws, ws_bytes, None)
@@ -60,7 +60,8 @@ def full_call(desc, x=A, wr=A, rb=None, gu=None, dn=None, sgu=None, sdn=None, ou
 def test_descriptor_validation():
     L = B.lib()
     n = ctypes.c_size_t()
-    assert L.moe_workspace_size(None, 1, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_layer_workspace_size(None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route_workspace_size(None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
     cases = [
         (B.layer_desc(-1, 256, 128, 16, 4), B.MOE_ERR_INVALID_ARGUMENT),
         (B.layer_desc(8, 0, 128, 16, 4), B.MOE_ERR_INVALID_ARGUMENT),
@@ -75,12 +76,20 @@ def test_descriptor_validation():
         (B.layer_desc(8, 256, 2112, 16, 4), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(1 << 27, 256, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),
         (B.layer_desc(1 << 20, 2048, 128, 16, 8), B.MOE_ERR_UNSUPPORTED_SHAPE),  # T*H*2 >= 2 GiB
+        # the pages' quant group is 64 weights; nothing else is taken
+        (B.layer_desc(8, 256, 128, 16, 4, group_size=0), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 256, 128, 16, 4, group_size=-64), B.MOE_ERR_INVALID_ARGUMENT),
+        (B.layer_desc(8, 256, 128, 16, 4, group_size=32), B.MOE_ERR_UNSUPPORTED_SHAPE),
+        (B.layer_desc(8, 256, 128, 16, 4, group_size=128), B.MOE_ERR_UNSUPPORTED_SHAPE),
     ]
     for d, want in cases:
-        assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == want
+        assert L.moe_layer_workspace_size(ctypes.byref(d), ctypes.byref(n)) == want
+        assert L.moe_route_workspace_size(ctypes.byref(d), ctypes.byref(n)) == want
+        assert L.moe_layer_workspace_size_ex(ctypes.byref(d), 0, ctypes.byref(n)) == want
         assert full_call(d, ws_bytes=1 << 40) == want
     d = B.layer_desc(8, 256, 128, 16, 4)
-    assert L.moe_workspace_size(ctypes.byref(d), 2, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_layer_workspace_size(ctypes.byref(d), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_layer_workspace_size_ex(ctypes.byref(d), 3, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_zero_tokens_is_a_noop_before_any_pointer_check():
@@ -89,13 +98,16 @@ def test_zero_tokens_is_a_noop_before_any_pointer_check():
     assert L.moe_layer_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 0,
                                None) == B.MOE_OK
     assert L.moe_route(ctypes.byref(d), None, None, None, None, None, 0, None) == B.MOE_OK
-    assert L.moe_combine(ctypes.byref(d), None, None, None, None) == B.MOE_OK
-    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 0, None, None, None, None, None, None) == B.MOE_OK
+    assert L.moe_combine(ctypes.byref(d), None, 0, None, None, None) == B.MOE_OK
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 0, None, None, None, None, None, None, 0, None) == B.MOE_OK
+    for mode in range(3):
+        assert L.moe_layer_forward_ex(ctypes.byref(d), mode, None, None, None, None, None, None, None, None, None,
+                                      None, 0, None) == B.MOE_OK
 
 
 def test_pointer_shape_alignment_and_workspace_errors():
     d = B.layer_desc(64, 256, 128, 16, 4)
-    need = B.moe_workspace_size(d, 1)
+    need = B.moe_layer_workspace_size(d)
     assert need > 0
     assert full_call(d, x=None) == B.MOE_ERR_INVALID_ARGUMENT
     assert full_call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
@@ -115,7 +127,18 @@ def test_pointer_shape_alignment_and_workspace_errors():
     L = B.lib()
     gu, dn = q4(16, 256, 256), q4(16, 256, 128)
     assert L.moe_layer_forward(ctypes.byref(d2), A, A, None, ctypes.byref(gu), ctypes.byref(dn), None, None, A,
-                               None, A, B.moe_workspace_size(d2, 1) - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+                               None, A, B.moe_layer_workspace_size(d2) - 1, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # the explicit combine modes check their own workspace sizes
+    for mode in range(3):
+        need_m = B.moe_layer_workspace_size_ex(d, mode)
+        call = lambda wsb, m=mode: L.moe_layer_forward_ex(  # noqa: E731
+            ctypes.byref(d), m, A, A, None, ctypes.byref(q4(16, 256, 256)), ctypes.byref(q4(16, 256, 128)),
+            ctypes.byref(q4(1, 256, 256)), ctypes.byref(q4(1, 256, 128)), A, None, A, wsb, None)
+        assert call(need_m - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_layer_forward_ex(ctypes.byref(d), 5, A, A, None, ctypes.byref(q4(16, 256, 256)),
+                                  ctypes.byref(q4(16, 256, 128)), ctypes.byref(q4(1, 256, 256)),
+                                  ctypes.byref(q4(1, 256, 128)), A, None, A, 1 << 40,
+                                  None) == B.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_entry_point_argument_errors():
@@ -125,21 +148,31 @@ def test_entry_point_argument_errors():
     w = q4(16, 256, 256)
     ws_ = q4(1, 256, 256)
     assert L.moe_grouped_gemm_q4(ctypes.byref(d), 7, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r), A,
-                                 None) == B.MOE_ERR_INVALID_ARGUMENT
+                                 None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), -1, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r), A,
+                                 None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_grouped_gemm_q4(ctypes.byref(d), 0, A, ctypes.byref(w), None, ctypes.byref(r), A,
-                                 None) == B.MOE_ERR_INVALID_ARGUMENT  # shared expert required
+                                 None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT  # shared expert required
     wd = q4(16, 256, 128)
-    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 1, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r), A,
-                                 None) == B.MOE_ERR_UNSUPPORTED_SHAPE  # gate/up tensor passed to down
-    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 1, MIS, ctypes.byref(wd), ctypes.byref(q4(1, 256, 128)),
-                                 ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
-    assert L.moe_combine(ctypes.byref(d), A, ctypes.byref(r), None, None) == B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_combine(ctypes.byref(d), MIS, ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+    wd_s = q4(1, 256, 128)
+    for mode in (1, 2, 3):
+        assert L.moe_grouped_gemm_q4(ctypes.byref(d), mode, A, ctypes.byref(w), ctypes.byref(ws_), ctypes.byref(r),
+                                     A, None, 0, None) == B.MOE_ERR_UNSUPPORTED_SHAPE  # gate/up tensor passed to down
+        assert L.moe_grouped_gemm_q4(ctypes.byref(d), mode, MIS, ctypes.byref(wd), ctypes.byref(wd_s),
+                                     ctypes.byref(r), A, None, 0, None) == B.MOE_ERR_MISALIGNED
+    # the fused combine reads the routing weights
+    r_now = B.RouteOutDesc(A, None, A, A, A, A, A, A)
+    assert L.moe_grouped_gemm_q4(ctypes.byref(d), 3, A, ctypes.byref(wd), ctypes.byref(wd_s), ctypes.byref(r_now),
+                                 A, None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(d), A, 0, ctypes.byref(r), None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(d), A, 2, ctypes.byref(r), A, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(d), MIS, 0, ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_combine(ctypes.byref(d), MIS, 1, ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
     assert L.moe_route(ctypes.byref(d), A, None, None, ctypes.byref(r), A, 1 << 20, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(r), None, 1 << 20, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_route(ctypes.byref(d), A, A, None, ctypes.byref(B.RouteOutDesc(A, A, A, A, A, A, A, MIS)), A,
                        1 << 20, None) == B.MOE_ERR_MISALIGNED
-    need = B.moe_workspace_size(d, 0)
+    need = B.moe_route_workspace_size(d)
     a256 = lambda n: (n + 255) // 256 * 256
     # approximate logits in 4 hidden-axis splits (a short prompt's logit grid is
     # split until it would pass one workgroup per CU)
@@ -156,18 +189,29 @@ def test_max_tiles_bound(T, E, K, shared):
 
 
 def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
-    small = B.moe_workspace_size(B.layer_desc(512, 2048, 512, 256, 8), 1)
-    big = B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 1)
+    small = B.moe_layer_workspace_size(B.layer_desc(512, 2048, 512, 256, 8))
+    d = B.layer_desc(4096, 2048, 512, 256, 8)
+    big = B.moe_layer_workspace_size(d)
     rows = 4096 * 9
-    assert big >= rows * 512 * 2 + rows * 2048 * 4
+    route = B.moe_route_workspace_size(d)
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    # routing results: ids, w, counts, offsets, sorted_idx, inv_pos, block map, n_tiles
+    results = (a256(4096 * 8 * 4) * 4 + a256(256 * 4) + a256(257 * 4)
+               + a256(B.moe_route_max_tiles(d) * 16) + a256(4))
+    h = rows * 512 * 2
+    # default: y staged as bf16
+    assert big == route + results + h + rows * 2048 * 2
+    assert B.moe_layer_workspace_size_ex(d, B.MOE_COMBINE_Y_BF16) == big
+    assert B.moe_layer_workspace_size_ex(d, B.MOE_COMBINE_Y_F32) == route + results + h + rows * 2048 * 4
+    # the fused combine stages no y at all
+    assert B.moe_layer_workspace_size_ex(d, B.MOE_COMBINE_FUSED) == route + results + h
     assert big > small
     # routing scratch: expert histograms [E][64-token groups rounded up to 4]
     # int32, 256 router-row norms, the piece-major router copy [H/8][E][8]
     # bf16 and approximate logits [T][E] fp32 (4096 tokens: one split)
-    assert B.moe_workspace_size(B.layer_desc(4096, 2048, 512, 256, 8), 0) == (
-        64 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 4096 * 256 * 4)
+    assert route == 64 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 4096 * 256 * 4
     # 512 tokens: 8 splits
-    assert B.moe_workspace_size(B.layer_desc(512, 2048, 512, 256, 8), 0) == (
+    assert B.moe_route_workspace_size(B.layer_desc(512, 2048, 512, 256, 8)) == (
         8 * 256 * 4 + 256 * 4 + 256 * 2048 * 2 + 8 * 512 * 256 * 4)
 
 
@@ -187,18 +231,18 @@ def test_ablation_entry_points_argument_errors():
     bw = B.Bf16Desc(A, 16, 256, 256)  # gate/up of H=256, I=128: N = 2I = 256, K = H = 256
     bs = B.Bf16Desc(A, 1, 256, 256)
     assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 7, A, ctypes.byref(bw), ctypes.byref(bs), ctypes.byref(r), A,
-                                   None) == B.MOE_ERR_INVALID_ARGUMENT
+                                   None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 0, A, ctypes.byref(bw), None, ctypes.byref(r), A,
-                                   None) == B.MOE_ERR_INVALID_ARGUMENT
+                                   None, 0, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 1, A, ctypes.byref(bw), ctypes.byref(bs), ctypes.byref(r), A,
-                                   None) == B.MOE_ERR_UNSUPPORTED_SHAPE
+                                   None, 0, None) == B.MOE_ERR_UNSUPPORTED_SHAPE
     assert L.moe_grouped_gemm_bf16(ctypes.byref(d), 0, A, ctypes.byref(B.Bf16Desc(MIS, 16, 256, 256)),
-                                   ctypes.byref(bs), ctypes.byref(r), A, None) == B.MOE_ERR_MISALIGNED
+                                   ctypes.byref(bs), ctypes.byref(r), A, None, 0, None) == B.MOE_ERR_MISALIGNED
     assert L.moe_grouped_gemm_bf16(ctypes.byref(B.layer_desc(0, 256, 128, 16, 4)), 0, A, ctypes.byref(bw),
-                                   ctypes.byref(bs), ctypes.byref(r), A, None) == B.MOE_OK
+                                   ctypes.byref(bs), ctypes.byref(r), A, None, 0, None) == B.MOE_OK
     # host-synchronizing layer: the same checks as moe_layer_forward
     gu, dn, sgu, sdn = q4(16, 256, 256), q4(16, 256, 128), q4(1, 256, 256), q4(1, 256, 128)
-    need = B.moe_workspace_size(d, 1)
+    need = B.moe_layer_workspace_size(d)
     call = lambda desc, ws_bytes=need, out=A: L.moe_layer_forward_host_sync(  # noqa: E731
         ctypes.byref(desc), A, A, None, ctypes.byref(gu), ctypes.byref(dn), ctypes.byref(sgu), ctypes.byref(sdn),
         out, None, A, ws_bytes, None)
@@ -213,7 +257,7 @@ def test_decode_entry_points_argument_errors():
     L = B.lib()
     d = B.layer_desc(4, 256, 128, 16, 4)
     gu, dn, sgu, sdn = q4(16, 256, 256), q4(16, 256, 128), q4(1, 256, 256), q4(1, 256, 128)
-    need = B.moe_workspace_size(d, 1)
+    need = B.moe_layer_workspace_size(d)
     assert L.moe_decode_router_prepare(ctypes.byref(d), None, A, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_decode_router_prepare(ctypes.byref(d), A, MIS, None) == B.MOE_ERR_MISALIGNED
     assert L.moe_decode_router_prepare(ctypes.byref(B.layer_desc(4, 100, 128, 16, 4)), A, A,
@@ -226,7 +270,7 @@ def test_decode_entry_points_argument_errors():
     assert call(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
     assert call(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
     big = B.layer_desc(B.MOE_DECODE_MAX_TOKENS + 1, 256, 128, 16, 4)
-    assert call(big, ws_bytes=B.moe_workspace_size(big, 1)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert call(big, ws_bytes=B.moe_layer_workspace_size(big)) == B.MOE_ERR_UNSUPPORTED_SHAPE
     assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
 
 

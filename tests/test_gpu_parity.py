@@ -95,45 +95,108 @@ def test_prefill512_full_parity():
     check_full(gen.make_layer(gen.WORKLOADS["prefill512"]), name="prefill512")
 
 
-def _sampled_check(inp, dl, out, routes, n_sample=48, full_route_chunks=(0,), seed=0):
+# The oracle's layer for the full-size workloads, computed once per session.
+_ORACLE = {}
+
+
+def oracle_layer(name, inp):
+    if name not in _ORACLE:
+        _announce(f"oracle layer on all {inp.shape.T} tokens of {name}")
+        _ORACLE[name] = oracle.layer_forward(inp)
+    return _ORACLE[name]
+
+
+def check_every_chunk(name, inp, dl, out, routes):
+    """Routing of every chunk bit-exact against the oracle's routing of the
+    same chunk, and every output element of the prompt against the oracle."""
     s = inp.shape
     T = s.T
     BM = B.moe_route_block_rows()
-    for ci in full_route_chunks:
-        c0 = ci * dl.chunk
+    for ci, c0 in enumerate(range(0, T, dl.chunk)):
         c1 = min(T, c0 + dl.chunk)
         _announce(f"oracle routing of chunk {ci} ({c1 - c0} tokens)")
         ref = oracle.route(np.ascontiguousarray(inp.x[c0:c1]), inp.w_router, s.K, rb=inp.router_bias)
         assert_route_equal(routes[ci], ref, s.K, s.E, c1 - c0, BM, dl.has_shared, oracle.block_map)
-    rng = np.random.default_rng(seed)
-    sample = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
-    _announce(f"oracle layer on {len(sample)} sampled tokens")
-    ref = oracle.layer_forward(inp, x=np.ascontiguousarray(inp.x[sample]))
-    return assert_out_close(out[sample], ref["out"])
+    return assert_out_close(out, oracle_layer(name, inp)["out"])
 
 
-def test_prefill4096_sampled_parity():
+def test_prefill4096_full_parity():
     inp = gen.make_layer(gen.WORKLOADS["prefill4096"])
     _announce("prefill4096 GPU run")
     dl, out, routes = run_layer(inp)
-    _sampled_check(inp, dl, out, routes)
+    check_every_chunk("prefill4096", inp, dl, out, routes)
 
 
-def test_skew2048_sampled_parity():
+def test_skew2048_full_parity():
     inp = gen.make_layer(gen.WORKLOADS["skew2048"])
     _announce("skew2048 GPU run")
     dl, out, routes = run_layer(inp)
     counts = host(routes[0]["counts"])
     assert counts.max() >= 200 and (counts <= 3).sum() >= 50  # uneven groups, many near-empty
-    _sampled_check(inp, dl, out, routes)
+    check_every_chunk("skew2048", inp, dl, out, routes)
 
 
-def test_long16384_chunked_parity():
+def test_long16384_chunked_full_parity():
     inp = gen.make_layer(gen.WORKLOADS["long16384"])
     _announce("long16384 GPU run in 4 chunks of 4096")
     dl, out, routes = run_layer(inp, chunk=4096)
     assert len(routes) == 4
-    _sampled_check(inp, dl, out, routes, n_sample=64, full_route_chunks=(0, 3))
+    check_every_chunk("long16384", inp, dl, out, routes)
+
+
+# ------------------------------------------------------------- combine modes
+
+MODES = {"y_f32": B.MOE_COMBINE_Y_F32, "y_bf16": B.MOE_COMBINE_Y_BF16, "fused": B.MOE_COMBINE_FUSED}
+
+
+def run_mode(inp, mode, chunk=None):
+    dl = DeviceLayer(inp, DEV, chunk=chunk, combine_mode=mode)
+    T = inp.shape.T
+    routes = [dl.new_route(min(dl.chunk, T - c0)) for c0 in range(0, T, dl.chunk)]
+    out = dl.forward(routes=routes)
+    torch.cuda.synchronize()
+    return dl, host(out), routes
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["tiny", "ragged_T300", "no_shared", "I512_E8", "E10_K3"])
+def test_combine_modes_small_full_parity(name, mode):
+    inp = gen.make_layer(SMALL[name])
+    s = inp.shape
+    _announce(f"combine mode {mode} {name} T={s.T}")
+    dl, out, routes = run_mode(inp, MODES[mode])
+    ref = oracle.layer_forward(inp)
+    assert_route_equal(routes[0], ref, s.K, s.E, s.T, B.moe_route_block_rows(), dl.has_shared, oracle.block_map)
+    assert_out_close(out, ref["out"])
+
+
+@pytest.mark.parametrize("mode", ["y_f32", "fused"])
+def test_combine_modes_prefill4096_full_parity(mode):
+    """The non-default modes at the benchmarked size, every element."""
+    inp = gen.make_layer(gen.WORKLOADS["prefill4096"])
+    _announce(f"prefill4096 combine mode {mode}")
+    dl, out, routes = run_mode(inp, MODES[mode])
+    check_every_chunk("prefill4096", inp, dl, out, routes)
+
+
+def test_fused_combine_long16384_chunks_full_parity():
+    """The fused mode clears `out` chunk by chunk inside its gate/up launch."""
+    inp = gen.make_layer(gen.WORKLOADS["long16384"])
+    _announce("long16384 fused combine in 4 chunks")
+    dl, out, routes = run_mode(inp, B.MOE_COMBINE_FUSED, chunk=4096)
+    check_every_chunk("long16384", inp, dl, out, routes)
+
+
+def test_modes_agree_and_bf16_staging_is_deterministic():
+    inp = gen.make_layer(SMALL["ragged_T300"])
+    _announce("modes against each other")
+    outs = {m: run_mode(inp, v)[1] for m, v in MODES.items()}
+    # y staged as fp32 and the fused adds differ only by fp32 summation order
+    assert_out_close(outs["fused"], outs["y_f32"], max_rel=1e-5, mean_rel=1e-6, what="fused vs y_f32")
+    # bf16 staging rounds each expert row once: within 2^-8 of the fp32 result
+    assert_out_close(outs["y_bf16"], outs["y_f32"], max_rel=4e-3, mean_rel=2e-3, what="y_bf16 vs y_f32")
+    again = run_mode(inp, B.MOE_COMBINE_Y_BF16)[1]
+    assert np.array_equal(again, outs["y_bf16"])
 
 
 # -------------------------------------------------------------- entry points
@@ -171,12 +234,31 @@ def test_entry_points_separately():
     B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN, h_in, dl.down.desc, dl.s_down.desc, rd, y)
     torch.cuda.synchronize()
     assert_out_close(host(y), ref["y"], max_rel=1e-4, mean_rel=1e-5, what="y")
+    # the same down GEMM storing bf16 y: each element the RNE bf16 of an fp32
+    # value within 1e-4 of the oracle's, so within 2^-9 relative of it
+    y16 = torch.empty((rows, s.H), dtype=torch.int16, device=DEV)
+    B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN_BF16, h_in, dl.down.desc, dl.s_down.desc, rd, y16)
+    torch.cuda.synchronize()
+    y16_h = gen.bf16_to_f32(host(y16))
+    assert_out_close(y16_h, ref["y"], max_rel=4e-3, mean_rel=2e-3, what="y bf16")
+    assert np.array_equal(host(y16), gen.bf16_bits(host(y)))  # the RNE bf16 of the fp32 mode's y
+    # the fused combine from the oracle's h: out = sum of weighted rows
+    out_f = torch.zeros((s.T, s.H), dtype=torch.float32, device=DEV)
+    B.moe_grouped_gemm_q4(d, B.MOE_GEMM_DOWN_COMBINE, h_in, dl.down.desc, dl.s_down.desc, rd, out_f)
+    torch.cuda.synchronize()
+    assert_out_close(host(out_f), ref["out"], max_rel=1e-4, mean_rel=1e-5, what="down+combine")
     # combine on the oracle's y and weights
     y_in = torch.from_numpy(ref["y"]).to(DEV)
     out = torch.empty((s.T, s.H), dtype=torch.float32, device=DEV)
     B.moe_combine(d, y_in, rd, out)
     torch.cuda.synchronize()
     assert_out_close(host(out), ref["out"], max_rel=1e-5, mean_rel=1e-6, what="combine")
+    # combine on bf16 y: exact bf16 inputs, fp32 sums; against the oracle's
+    # out within the bf16 rounding of y
+    y_in16 = torch.from_numpy(gen.bf16_bits(ref["y"]).view(np.int16)).to(DEV)
+    B.moe_combine(d, y_in16, rd, out, y_dtype=B.MOE_DTYPE_BF16)
+    torch.cuda.synchronize()
+    assert_out_close(host(out), ref["out"], max_rel=4e-3, mean_rel=2e-3, what="combine bf16 y")
 
 
 def test_zero_tokens_launches_nothing():
