@@ -63,7 +63,6 @@ namespace moeq4 {
 namespace {
 using namespace gemm;
 
-constexpr int BM = kTileRows;    // max rows per tile (256 = 16 MFMA subtiles)
 constexpr int BK = 64;           // reduction columns per stage (= quant group)
 constexpr int NWAVES = 4;        // one wave per SIMD
 constexpr int NT = 64 * NWAVES;  // lanes per workgroup
@@ -119,6 +118,7 @@ struct TileCtx {
   int row0, nrows;
   int ocol[NS];
   bool jval[NS];
+  int col0;             // first output column of the workgroup's slice (h or y)
   uint32_t wd_off[1];   // per-lane offset of the direct-to-LDS code load (short-tile form)
 };
 
@@ -187,7 +187,7 @@ __device__ __forceinline__ void activation_offsets(const GemmArgs& g, const Tile
 // Epilogue: the lane holds output row 16m + ln, columns 4*lg..4*lg+3 of each
 // subtile, written as one vector store per subtile.
 template <bool kGateUp, int MSUB>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, const f32x4 (&acc)[MSUB][NS]) {
+__device__ __forceinline__ void store_tile_direct(const GemmArgs& g, const TileCtx& t, const f32x4 (&acc)[MSUB][NS]) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int r_in = ln;
@@ -225,6 +225,82 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, 
         for (int j = 0; j < NS; ++j)
           if (t.jval[j]) store_down4(g, dr, t.ocol[j] - ln + 4 * lg, acc[m][j]);
       }
+    }
+  }
+}
+
+// SwiGLU of four gate/up accumulator pairs, as two dwords of bf16 h.
+__device__ __forceinline__ u32x2 swiglu4(const f32x4& gt, const f32x4& up) {
+  uint32_t hv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float o[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float gv = gt[2 * i + q], uv = up[2 * i + q];
+      o[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+    }
+    hv[i] = pack_bf16x2(o[0], o[1]);
+  }
+  return u32x2{hv[0], hv[1]};
+}
+
+// Epilogue for bf16 outputs (gate/up h, down y in bf16).  A lane holds four
+// consecutive columns of 16 rows per subtile, so direct stores are 8 bytes
+// spread over 16 rows; instead the tile goes through LDS (free once the last
+// stage has been read) and leaves as 16-byte stores that cover the slice's
+// whole row segment: 128 B of h or 256 B of y per row, full cache lines.
+// y is written with non-temporal stores: it is far larger than L2 and is
+// read back only by the combine, while h is read by the down GEMM next.
+// LDS layout: row r of the slice in array r / RPA, its 16-byte chunk c at
+// chunk c ^ (r % CH), so the 16 rows one write instruction touches fall on
+// different banks.
+template <bool kGateUp, int MSUB>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, const LdsQ& L,
+                                           const f32x4 (&acc)[MSUB][NS]) {
+  if (!kGateUp && g.out_mode != kOutBf16) {
+    store_tile_direct<kGateUp, MSUB>(g, t, acc);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  constexpr int OC = kGateUp ? BN / 2 : BN;  // bf16 output columns of the slice
+  constexpr int CH = OC / 8;                 // 16-byte chunks per row
+  constexpr int RPA = kQElems / OC;          // slice rows per LDS array
+  static_assert(MSUB * 16 <= 4 * RPA, "the staged tile fits the four arrays");
+  auto at = [&](int r, int c) { return lds_q(L, r / RPA) + (r % RPA) * OC + ((c ^ (r % CH)) * 8); };
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave's ring DMAs landed and every wave is past its last LDS read
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m) {
+    const int r = m * 16 + ln;
+    if constexpr (kGateUp) {
+      const int col = wave * (WN / 2) + 4 * lg;  // h column in the slice
+      *reinterpret_cast<u32x2*>(at(r, col / 8) + (col & 4)) = swiglu4(acc[m][0], acc[m][1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int col = wave * WN + 16 * j + 4 * lg;
+        const f32x4 v = acc[m][j];
+        *reinterpret_cast<u32x2*>(at(r, col / 8) + (col & 4)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* out = reinterpret_cast<uint16_t*>(g.c);
+  const int ld = kGateUp ? g.I : g.N;  // row pitch of h or y
+  const int ncol = ld - t.col0;        // columns of the slice inside the matrix
+#pragma unroll
+  for (int it = 0; it < (MSUB * 16 * CH + NT - 1) / NT; ++it) {
+    const int idx = tid + NT * it;
+    const int r = idx / CH, c = idx % CH;
+    if (r < t.nrows && 8 * c < ncol) {
+      u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + r) * ld + t.col0 + 8 * c);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(at(r, c));
+      if constexpr (kGateUp) *dst = v;
+      else __builtin_nontemporal_store(v, dst);
     }
   }
 }
@@ -379,7 +455,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, c
   if (kt < nk) stage(kNext, kSlot1, kt, bq[1], bq[0]);
   wait_vmcnt<0>();  // no direct-to-LDS write outlives the tile
 
-  store_tile<kGateUp, MSUB>(g, t, acc);
+  store_tile<kGateUp, MSUB>(g, t, L, acc);
 }
 
 // Short tiles (<= 4 row subtiles) have little matrix work per stage, so the
@@ -508,7 +584,7 @@ __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx&
   if (kt + 1 < nk) stage(kS1, kt + 1);
   if (kt + 2 < nk) stage(kS2, kt + 2);
   wait_vmcnt<0>();  // no direct-to-LDS write outlives the tile
-  store_tile<kGateUp, MSUB>(g, t, acc);
+  store_tile<kGateUp, MSUB>(g, t, L, acc);
 }
 
 template <bool kGateUp, bool kBf16W>
@@ -608,12 +684,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
     t.sb_half = (BN / 2) * gpr * 2 / 16;
     t.sb_src[0] = (uint32_t)(nb * (BN / 2)) * gpr * 2u;
     t.sb_src[1] = (uint32_t)(g.I + nb * (BN / 2)) * gpr * 2u;
+    t.col0 = nb * (BN / 2);
   } else {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       t.ocol[j] = nb * BN + wave * WN + 16 * j + ln;
       t.sb_row[j] = wave * WN + 16 * j + ln;
     }
+    t.col0 = nb * BN;
     // one contiguous range of 128 rows, split in two halves of 64
     t.sb_half = (BN / 2) * gpr * 2 / 16;
     t.sb_src[0] = (uint32_t)(nb * BN) * gpr * 2u;

@@ -103,7 +103,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 // s_waitcnt lgkmcnt(0) alone (vmcnt 63 and expcnt 7 leave those counters
 // unconstrained).
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
 // Order-preserving map of an fp32 value to uint32 (-0 is taken as +0 first,
 // so equal values get equal keys) and its inverse.
 __device__ __forceinline__ uint32_t fkey(float f) {
