@@ -90,7 +90,8 @@ def run_gdn(args, shape, torch, B, gen):
     if not args.no_cpu_baseline:
         import oracle.gdn as G
 
-        threads = min(int(os.environ.get("OMP_NUM_THREADS") or (os.cpu_count() or 1)), os.cpu_count() or 1, HV)
+        G.set_threads(os.cpu_count() or 1)  # every host core; the oracle splits over value heads
+        threads = min(os.cpu_count() or 1, HV)
         t1 = time.perf_counter()
         G.scan(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.state_in)
         dt = time.perf_counter() - t1
@@ -155,7 +156,8 @@ def run_gqa(args, shape, torch, B, gen):
     if not args.no_cpu_baseline:
         import oracle.gqa as OA
 
-        threads = min(int(os.environ.get("OMP_NUM_THREADS") or (os.cpu_count() or 1)), os.cpu_count() or 1, HQ)
+        OA.set_threads(os.cpu_count() or 1)  # every host core; the oracle splits over query heads
+        threads = min(os.cpu_count() or 1, HQ)
         t1 = time.perf_counter()
         reps = 0
         while True:
@@ -195,6 +197,28 @@ def load_traffic(kernel: str, workload: str):
     return ent["hbm_bytes_per_launch"]
 
 
+def measure_temp_memory(torch, B, dl, chunks, out):
+    """Peak temporary device memory of the layer over the whole prompt: the
+    workspace moe_layer_forward needs is allocated inside a
+    torch.cuda.max_memory_allocated window and the prompt runs chunk by chunk
+    through it (routing results inside the workspace); the library itself
+    allocates nothing."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    nbytes = B.moe_layer_workspace_size(dl.desc(dl.chunk))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=out.device)
+    for c0, c1 in chunks:
+        B.moe_layer_forward(dl.desc(c1 - c0), dl.x[c0:c1], dl.w_router, dl.router_bias, dl.gate_up.desc,
+                            dl.down.desc, dl.s_gate_up.desc if dl.has_shared else None,
+                            dl.s_down.desc if dl.has_shared else None, out[c0:c1], None, ws, nbytes)
+    torch.cuda.synchronize()
+    delta = torch.cuda.max_memory_allocated() - base
+    del ws
+    return {"workspace_bytes": nbytes, "peak_allocated_delta_bytes": int(delta), "chunks": len(chunks),
+            "chunk_tokens": dl.chunk}
+
+
 def copy_calibration(args, torch) -> int:
     """A plain copy of known size: reads and writes n bytes per launch."""
     n = args.copy_calibration_mib << 20
@@ -214,7 +238,7 @@ def copy_calibration(args, torch) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill4096",
                     help="prefill4096 (default), prefill512, skew2048, long16384, tiny; decode1, decode4, "
@@ -372,13 +396,18 @@ def main() -> int:
     # second, untimed pass records all phase events for the breakdown.
     gu = names.index("gemm_gate_up")
     evs = new_events()
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        step_evs[s][0].record(stream)
         step(evs[s], only=(gu, gu + 1))
+        step_evs[s][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gu_ms_timed = phase_times(evs, ["gemm_gate_up"])["gemm_gate_up"]
+    step_ms = [a.elapsed_time(b) for a, b in step_evs]
     evs_all = new_events()
     for s in range(args.steps):
         step(evs_all[s])
@@ -402,7 +431,7 @@ def main() -> int:
     Tc = float(np.mean([c1 - c0 for c0, c1 in chunks]))
     Rc = Tc * K
     route_bytes = Tc * H * 2 + E * H * 2 + Rc * 8 + 2 * Rc * 4 + (2 * E + 1) * 4
-    comb_bytes = rows_m * H * 4 + Tc * H * 4 + Rc * 8
+    comb_bytes = rows_m * H * 2 + Tc * H * 4 + Rc * 8  # bf16 y rows in, fp32 out
 
     def rate(b, ms):
         return round(b / (ms * 1e-3) / 1e9, 1)
@@ -423,6 +452,9 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
     total_flop = flop_gu * len(chunks) + flop_dn * len(chunks)
+    dn_ms = kernels_ms["gemm_down"]
+    med_step_ms = float(np.median(step_ms))
+    temp_mem = measure_temp_memory(torch, B, dl, chunks, out)
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -453,12 +485,19 @@ def main() -> int:
             "traffic": traffic,
             "flop_per_launch": flop_gu,
             "avg_launch_ms": round(gu_ms, 4),
+            # the other GEMM and the whole layer against the same bf16 dense peak
+            "gemm_down_frac": round(flop_dn / (dn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm_down_avg_launch_ms": round(dn_ms, 4),
+            "layer_gemm_frac": round(total_flop / (med_step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
         "kernels": kernels,
         "kernels_note": "per-phase HIP-event means from a second pass of the same steps with an event between "
                         "every phase; the timed pass brackets only the gate/up GEMM",
         "layer_gemm_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
-        "workspace_bytes_layer_forward": dl.ws_bytes,
+        "step_ms_median": round(med_step_ms, 4),
+        "step_ms_mean": round(float(np.mean(step_ms)), 4),
+        "step_ms_note": "HIP events on the launch stream around each timed step",
+        "temporary_memory": temp_mem,
         "nonempty_experts_last_chunk": int((counts_last > 0).sum()),
     }
 
@@ -466,7 +505,7 @@ def main() -> int:
         import oracle
 
         S = min(args.cpu_sample_tokens, T)
-        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS") or 16))
+        nthreads = os.cpu_count() or 1  # every host core
         xs = np.ascontiguousarray(inp.x[:S])
         t1 = time.perf_counter()
         oracle.layer_forward(inp, x=xs, nthreads=nthreads)
@@ -538,7 +577,7 @@ def run_decode(args, shape, torch, B, gen):
     if not args.no_cpu_baseline:
         import oracle
 
-        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS") or 16))
+        nthreads = os.cpu_count() or 1  # every host core
         t1 = time.perf_counter()
         reps = 0
         while True:

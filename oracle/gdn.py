@@ -50,6 +50,11 @@ def _p(a):
     return ctypes.c_void_p(a.ctypes.data)
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's next calls (threading only)."""
+    lib().gdn_ref_set_threads(ctypes.c_int(int(n)))
+
+
 def scan(q, k, v, alpha, beta, state_in=None):
     """Gated delta rule over T tokens.
 

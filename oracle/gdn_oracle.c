@@ -28,6 +28,7 @@
  * alpha, beta and the initial state are fp32.
  */
 #include <stddef.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -91,4 +92,10 @@ int gdn_ref_scan(int T, int HK, int HV, int DK, int DV, const uint16_t* q, const
     free(qq);
   }
   return bad ? -1 : 0;
+}
+
+/* OpenMP threads of the next calls (n <= 0 leaves the default).  Threading
+ * only: the arithmetic and its order per output are the same for any n. */
+void gdn_ref_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
 }

@@ -48,6 +48,11 @@ def _p(a):
     return ctypes.c_void_p(a.ctypes.data)
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's next calls (threading only)."""
+    lib().gqa_ref_set_threads(ctypes.c_int(int(n)))
+
+
 def decode(L, q, k_blocks, v_blocks, HKV, scale):
     """q: uint16 bf16 bits [HQ, D]; k_blocks: [nb, HKV, 32, D]; v_blocks:
     [nb, HKV, D, 32] (nb >= ceil(L/32)).  Returns out float64 [HQ, D]."""

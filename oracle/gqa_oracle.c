@@ -18,6 +18,7 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -77,4 +78,10 @@ int gqa_ref_decode(int L, int HQ, int HKV, int D, double scale, const uint16_t* 
     free(s);
   }
   return bad ? -1 : 0;
+}
+
+/* OpenMP threads of the next calls (n <= 0 leaves the default).  Threading
+ * only: the arithmetic and its order per output are the same for any n. */
+void gqa_ref_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
 }

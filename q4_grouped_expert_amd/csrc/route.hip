@@ -47,16 +47,11 @@ constexpr int kSelTokens = 16;                    // tokens per selection workgr
 constexpr int kXfStride = MOE_MAX_REDUCTION + 4;  // fp32 per token row in LDS (16-byte pad)
 }  // namespace
 
-// ||w_e||_2 of every router row, and the router matrix copied piece-major:
+// ||w_e||_2 of router row e, and the row copied piece-major:
 // wt[p][e][0..7] = Wr[e][8p .. 8p+7] (p < H/8), so that piece p of
-// neighbouring experts shares a cache line.  One wave per expert; the
-// workgroups also clear the expert histograms that the selection kernel
-// accumulates into.
-__global__ __launch_bounds__(64) void route_wprep_kernel(const uint16_t* __restrict__ wr, int H, int E, float* wn,
-                                                         uint16_t* __restrict__ wt, int32_t* __restrict__ hist,
-                                                         int hist_len) {
-  const int e = blockIdx.x, lane = threadIdx.x;
-  for (int i = e * 64 + lane; i < hist_len; i += gridDim.x * 64) hist[i] = 0;
+// neighbouring experts shares a cache line.  One wave.
+__device__ __forceinline__ void router_row_prep(const uint16_t* __restrict__ wr, int H, int E, int e, int lane,
+                                                float* __restrict__ wnorm, uint16_t* __restrict__ wt) {
   // H <= 2048: at most four 16-byte pieces per lane, all loaded before use
   u32x4 v[MOE_MAX_REDUCTION / 512];
 #pragma unroll
@@ -78,7 +73,7 @@ __global__ __launch_bounds__(64) void route_wprep_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) wn[e] = sqrtf(s);
+  if (lane == 0) wnorm[e] = sqrtf(s);
 }
 
 namespace {
@@ -136,12 +131,21 @@ __device__ __forceinline__ uint64_t lanes_below() {
 // L2.  Ids past the last token tile exit at once.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb, int neb, int nsplit,
-                                                           float* __restrict__ alog) {
+                                                           float* __restrict__ alog, float* __restrict__ wnorm,
+                                                           uint16_t* __restrict__ wt, int32_t* __restrict__ hist,
+                                                           int hist_len) {
   constexpr int kRows = 2 * kLgTile;            // token rows, then router rows
   constexpr int kSlot = kRows * kLgK;           // bf16 elements per ring slot
   __shared__ __attribute__((aligned(16))) uint16_t ring[3 * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // What the selection kernel (the next launch) reads besides the logits:
+  // cleared expert histograms, router-row norms and the piece-major router
+  // copy, spread over the whole grid (wave 0 of block b takes experts b,
+  // b + grid, ...), before any block exits.
+  for (int i = blockIdx.x * 256 + tid; i < hist_len; i += gridDim.x * 256) hist[i] = 0;
+  if (wave == 0)
+    for (int e = blockIdx.x; e < a.E; e += gridDim.x) router_row_prep(a.w_router, a.H, a.E, e, lane, wnorm, wt);
   const int ln = lane & 15, lg = lane >> 4;
   // split of the hidden axis outermost, then the token-tile / expert-tile
   // order described above
@@ -843,15 +847,12 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   float* wn = reinterpret_cast<float*>(base + L.wn);
   uint16_t* wt = reinterpret_cast<uint16_t*>(base + L.wt);
   float* alog = reinterpret_cast<float*>(base + L.alog);
-  hipLaunchKernelGGL(route_wprep_kernel, dim3(a.E), dim3(64), 0, stream, a.w_router, a.H, a.E, wn, wt, hist,
-                     ngp * a.E);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   const int ntb = (a.T + kLgTile - 1) / kLgTile, neb = (a.E + kLgTile - 1) / kLgTile;
   const int ns = logit_splits(a.T, a.H, a.E);
   hipLaunchKernelGGL(route_logits_kernel, dim3((ntb + 7) / 8 * 8 * neb * ns), dim3(256), 0, stream, a, ntb, neb, ns,
-                     alog);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+                     alog, wn, wt, hist, ngp * a.E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   const dim3 sel_grid((a.T + kSelTokens - 1) / kSelTokens);
   switch (ns) {
     case 1: hipLaunchKernelGGL(route_select_kernel<1>, sel_grid, dim3(256), 0, stream, a, alog, wn, wt, hist, ngp); break;
