@@ -24,6 +24,10 @@ extern "C" {
 #endif
 
 #define MOE_DECODE_MAX_TOKENS 16
+/* Size of the scratch array behind moe_decode_forward_noalloc: enough for
+ * every shape the decode path takes (T <= 16, H and I <= 2048, E <= 256,
+ * top_k <= 16). */
+#define MOE_DECODE_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Write the router matrix once per model in the layout the decode router
  * reads: w_router_pm[h/4][e][i] = (fp32) w_router[e][4*(h/4) + i], i < 4
@@ -44,6 +48,24 @@ int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const floa
                        const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
                        const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
                        const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_decode_forward with no workspace argument.  Its scratch is a
+ * library-owned device array of MOE_DECODE_NOALLOC_SCRATCH_BYTES bytes,
+ * one per GPU, held until the process ends; the call allocates and frees
+ * nothing.  Arguments otherwise as for moe_decode_forward.  Calls on one GPU
+ * share that array, so calls that overlap on one GPU (different streams, or
+ * different host threads) race and give unspecified results; calls in order
+ * on one stream are safe.  Nothing in the array needs to start at zero.
+ * Errors: as moe_decode_forward; MOE_ERR_WORKSPACE_TOO_SMALL if the shape's
+ * scratch exceeds the array; MOE_ERR_HIP if the array's device address
+ * cannot be taken. */
+int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+                               const float* router_bias, const moe_q4_tensor* w_gate_up,
+                               const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
+                               const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null,
+                               void* stream);
 
 #ifdef __cplusplus
 }

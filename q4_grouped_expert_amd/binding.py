@@ -107,6 +107,9 @@ SIGNATURES = {
     "moe_decode_forward": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
                                           ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
                                           c_p, ctypes.POINTER(RouteOutDesc), c_p, ctypes.c_size_t, c_p]),
+    "moe_decode_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(LayerDesc), c_p, c_p, c_p, ctypes.POINTER(Q4Desc),
+                                                  ctypes.POINTER(Q4Desc), ctypes.POINTER(Q4Desc),
+                                                  ctypes.POINTER(Q4Desc), c_p, ctypes.POINTER(RouteOutDesc), c_p]),
     # the Gated DeltaNet prefill scan (gdn_scan.h)
     "gdn_prefill_scan": (ctypes.c_int, [ctypes.POINTER(GdnScanDesc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     # batch-1 GQA decode attention (gqa_decode.h)
@@ -116,6 +119,7 @@ SIGNATURES = {
 }
 GQA_BLOCK = 32
 MOE_DECODE_MAX_TOKENS = 16
+MOE_DECODE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -288,6 +292,15 @@ def moe_decode_forward(desc, x, w_router_pm, router_bias, w_gate_up: Q4Desc, w_d
     _chk("moe_decode_forward", lib().moe_decode_forward(
         ctypes.byref(desc), _ptr(x), _ptr(w_router_pm), _ptr(router_bias), byref(w_gate_up), byref(w_down),
         byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_decode_forward_noalloc(desc, x, w_router_pm, router_bias, w_gate_up: Q4Desc, w_down: Q4Desc,
+                               shared_gate_up: Optional[Q4Desc], shared_down: Optional[Q4Desc], out,
+                               route: Optional[RouteOutDesc], stream=None):
+    byref = lambda d: ctypes.byref(d) if d is not None else None  # noqa: E731
+    _chk("moe_decode_forward_noalloc", lib().moe_decode_forward_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router_pm), _ptr(router_bias), byref(w_gate_up), byref(w_down),
+        byref(shared_gate_up), byref(shared_down), _ptr(out), byref(route), _stream(stream)))
 
 
 def gdn_desc(T, HK, HV, DK, DV) -> GdnScanDesc:

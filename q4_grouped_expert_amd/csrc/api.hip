@@ -4,11 +4,42 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "moe_q4_ablation.h"
 #include "moe_q4_decode.h"
 
 using namespace moeq4;
+
+// Scratch of moe_decode_forward_noalloc: a file-scope device array, one copy
+// per GPU for the life of the process.  Host code never uses its name as an
+// address (that is a host-side stand-in); it takes each device's address
+// once with hipGetSymbolAddress and uses that.
+constexpr size_t kScratchBytes = MOE_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once taken
+
+// The current device's copy of `scratch` (taken on its first use there).
+int device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -203,7 +234,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
                   const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                   const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null, void* ws,
                   size_t ws_bytes, void* stream, bool host_sync, const float* decode_wf = nullptr,
-                  int combine_mode = kDefaultCombine) {
+                  int combine_mode = kDefaultCombine, bool use_scratch = false) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (combine_mode != MOE_COMBINE_Y_F32 && combine_mode != MOE_COMBINE_Y_BF16 && combine_mode != MOE_COMBINE_FUSED)
@@ -211,7 +242,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   const bool decode = decode_wf != nullptr;
   if (decode && desc->T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (desc->T == 0) return MOE_OK;
-  if (!x || !w_router || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !w_router || !out || (!ws && !use_scratch)) return MOE_ERR_INVALID_ARGUMENT;
   if ((rc = check_q4(w_gate_up, desc->E, 2 * desc->I, desc->H))) return rc;
   if ((rc = check_q4(w_down, desc->E, desc->H, desc->I))) return rc;
   if (desc->has_shared) {
@@ -221,10 +252,16 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
     shared_gate_up = shared_down = nullptr;
   }
   if (route_or_null && (rc = check_route_out(route_or_null))) return rc;
-  if (misaligned(x) || misaligned(w_router) || misaligned(out) || misaligned(ws) ||
+  if (misaligned(x) || misaligned(w_router) || misaligned(out) || (!use_scratch && misaligned(ws)) ||
       (router_bias && misaligned(router_bias)))
     return MOE_ERR_MISALIGNED;
   const Layout L = layout_of(desc, combine_mode);
+  if (use_scratch) {
+    // the library's own scratch instead of a caller workspace
+    if (L.total > kScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if ((rc = device_scratch(&ws))) return rc;
+    ws_bytes = kScratchBytes;
+  }
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   char* base = reinterpret_cast<char*>(ws);
@@ -438,6 +475,18 @@ int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const floa
   // in for it in the shared argument checks
   return layer_forward(desc, x, reinterpret_cast<const uint16_t*>(w_router_pm), router_bias, w_gate_up, w_down,
                        shared_gate_up, shared_down, out, route_or_null, ws, ws_bytes, stream, false, w_router_pm);
+}
+
+int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+                               const float* router_bias, const moe_q4_tensor* w_gate_up,
+                               const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
+                               const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null,
+                               void* stream) {
+  if (!w_router_pm) return MOE_ERR_INVALID_ARGUMENT;
+  if (misaligned(w_router_pm)) return MOE_ERR_MISALIGNED;
+  return layer_forward(desc, x, reinterpret_cast<const uint16_t*>(w_router_pm), router_bias, w_gate_up, w_down,
+                       shared_gate_up, shared_down, out, route_or_null, nullptr, 0, stream, false, w_router_pm,
+                       kDefaultCombine, true);
 }
 
 int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null, uint16_t* out, void* stream) {

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(HEADERS) == 5 and len(names) == 19
+    assert len(HEADERS) == 5 and len(names) == 20
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -272,6 +272,20 @@ def test_decode_entry_points_argument_errors():
     big = B.layer_desc(B.MOE_DECODE_MAX_TOKENS + 1, 256, 128, 16, 4)
     assert call(big, ws_bytes=B.moe_layer_workspace_size(big)) == B.MOE_ERR_UNSUPPORTED_SHAPE
     assert call(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
+    # the allocation-free variant: the same checks, before its scratch is touched
+    na = lambda desc, wf=A, out=A, x=A: L.moe_decode_forward_noalloc(  # noqa: E731
+        ctypes.byref(desc), x, wf, None, ctypes.byref(gu), ctypes.byref(dn), ctypes.byref(sgu), ctypes.byref(sdn),
+        out, None, None)
+    assert na(d, wf=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert na(d, wf=MIS) == B.MOE_ERR_MISALIGNED
+    assert na(d, out=None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert na(d, x=MIS) == B.MOE_ERR_MISALIGNED
+    assert na(big) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    assert na(B.layer_desc(0, 256, 128, 16, 4)) == B.MOE_OK
+    assert na(B.layer_desc(4, 256, 128, 16, 4, group_size=32)) == B.MOE_ERR_UNSUPPORTED_SHAPE
+    # every shape the decode path takes fits the scratch array
+    worst = B.layer_desc(B.MOE_DECODE_MAX_TOKENS, 2048, 2048, 256, 16)
+    assert B.moe_layer_workspace_size(worst) <= B.MOE_DECODE_NOALLOC_SCRATCH_BYTES
 
 
 def test_gdn_scan_argument_errors():
