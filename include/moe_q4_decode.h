@@ -30,9 +30,11 @@ extern "C" {
 #define MOE_DECODE_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Write the router matrix once per model in the layout the decode router
- * reads: w_router_pm[h/4][e][i] = (fp32) w_router[e][4*(h/4) + i], i < 4
- * (E * H fp32, device, caller-owned).  desc supplies H and E (T unused). */
-int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, float* w_router_pm,
+ * reads, piece-major: w_router_pm[p][e][i] = w_router[e][8*p + i] for
+ * p < H/8, i < 8 (E * H bf16, device, caller-owned), so that piece p of 64
+ * consecutive experts is 1 KB of consecutive memory.  desc supplies H and E
+ * (T unused). */
+int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, uint16_t* w_router_pm,
                               void* stream);
 
 /* The layer for 1 <= T <= MOE_DECODE_MAX_TOKENS tokens (T == 0: no-op):
@@ -44,7 +46,7 @@ int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_rout
  * moe_decode_router_prepare.  Other arguments, the workspace
  * (moe_layer_workspace_size bytes) and the combine mode as for
  * moe_layer_forward. */
-int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router_pm,
                        const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
                        const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
                        const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream);
@@ -61,7 +63,7 @@ int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const floa
  * Errors: as moe_decode_forward; MOE_ERR_WORKSPACE_TOO_SMALL if the shape's
  * scratch exceeds the array; MOE_ERR_HIP if the array's device address
  * cannot be taken. */
-int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router_pm,
                                const float* router_bias, const moe_q4_tensor* w_gate_up,
                                const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                                const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null,

@@ -46,7 +46,7 @@ namespace {
 constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
 // Tokens up to which the decode path runs the expert FFN as split-reduction
 // GEMVs instead of the tiled grouped GEMM.
-constexpr int kDecodeGemvMaxTokens = 1;
+constexpr int kDecodeGemvMaxTokens = 4;
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -228,18 +228,18 @@ int check_bf16(const moe_bf16_tensor* t, int n_exp, int N, int K) {
 
 // The layer for one chunk.  host_sync: after routing, copy n_tiles to the
 // host, wait for the stream and size the GEMM grids from it.
-// decode_wf: the decode path (T <= 16) with the prepared fp32 router copy;
+// decode_wt: the decode path (T <= 16) with the prepared piece-major router copy;
 // w_router is then unused.
 int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                   const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                   const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null, void* ws,
-                  size_t ws_bytes, void* stream, bool host_sync, const float* decode_wf = nullptr,
+                  size_t ws_bytes, void* stream, bool host_sync, const uint16_t* decode_wt = nullptr,
                   int combine_mode = kDefaultCombine, bool use_scratch = false) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (combine_mode != MOE_COMBINE_Y_F32 && combine_mode != MOE_COMBINE_Y_BF16 && combine_mode != MOE_COMBINE_FUSED)
     return MOE_ERR_INVALID_ARGUMENT;
-  const bool decode = decode_wf != nullptr;
+  const bool decode = decode_wt != nullptr;
   if (decode && desc->T > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (desc->T == 0) return MOE_OK;
   if (!x || !w_router || !out || (!ws && !use_scratch)) return MOE_ERR_INVALID_ARGUMENT;
@@ -284,7 +284,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   if (decode) {
     DecodeRouteArgs a;
     a.x = x;
-    a.wf = decode_wf;
+    a.wt = decode_wt;
     a.router_bias = router_bias;
     a.logits = reinterpret_cast<float*>(base + L.hist);  // the routing scratch holds T*E fp32 and more
     a.T = desc->T;
@@ -456,7 +456,7 @@ int moe_layer_forward_host_sync(const moe_layer_desc* desc, const uint16_t* x, c
                        route_or_null, ws, ws_bytes, stream, true);
 }
 
-int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, float* w_router_pm,
+int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_router, uint16_t* w_router_pm,
                               void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
@@ -465,7 +465,7 @@ int moe_decode_router_prepare(const moe_layer_desc* desc, const uint16_t* w_rout
   return hip_status(launch_decode_prep(w_router, desc->H, desc->E, w_router_pm, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router_pm,
                        const float* router_bias, const moe_q4_tensor* w_gate_up, const moe_q4_tensor* w_down,
                        const moe_q4_tensor* shared_gate_up, const moe_q4_tensor* shared_down, float* out,
                        const moe_route_out* route_or_null, void* ws, size_t ws_bytes, void* stream) {
@@ -473,20 +473,19 @@ int moe_decode_forward(const moe_layer_desc* desc, const uint16_t* x, const floa
   if (misaligned(w_router_pm)) return MOE_ERR_MISALIGNED;
   // the bf16 router matrix is not read on this path; the prepared copy stands
   // in for it in the shared argument checks
-  return layer_forward(desc, x, reinterpret_cast<const uint16_t*>(w_router_pm), router_bias, w_gate_up, w_down,
-                       shared_gate_up, shared_down, out, route_or_null, ws, ws_bytes, stream, false, w_router_pm);
+  return layer_forward(desc, x, w_router_pm, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
+                       route_or_null, ws, ws_bytes, stream, false, w_router_pm);
 }
 
-int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const float* w_router_pm,
+int moe_decode_forward_noalloc(const moe_layer_desc* desc, const uint16_t* x, const uint16_t* w_router_pm,
                                const float* router_bias, const moe_q4_tensor* w_gate_up,
                                const moe_q4_tensor* w_down, const moe_q4_tensor* shared_gate_up,
                                const moe_q4_tensor* shared_down, float* out, const moe_route_out* route_or_null,
                                void* stream) {
   if (!w_router_pm) return MOE_ERR_INVALID_ARGUMENT;
   if (misaligned(w_router_pm)) return MOE_ERR_MISALIGNED;
-  return layer_forward(desc, x, reinterpret_cast<const uint16_t*>(w_router_pm), router_bias, w_gate_up, w_down,
-                       shared_gate_up, shared_down, out, route_or_null, nullptr, 0, stream, false, w_router_pm,
-                       kDefaultCombine, true);
+  return layer_forward(desc, x, w_router_pm, router_bias, w_gate_up, w_down, shared_gate_up, shared_down, out,
+                       route_or_null, nullptr, 0, stream, false, w_router_pm, kDefaultCombine, true);
 }
 
 int moe_dequant_q4_to_bf16(const moe_q4_tensor* w, const int32_t* counts_or_null, uint16_t* out, void* stream) {

@@ -99,13 +99,13 @@ hipError_t launch_dequant(const DequantArgs& d, hipStream_t stream);
 // (once per model), router + grouping, split-reduction expert GEMVs.
 struct DecodeRouteArgs {
   const uint16_t* x;
-  const float* wf;  // [H/4][E][4] fp32
+  const uint16_t* wt;  // [H/8][E][8] bf16, piece-major
   const float* router_bias;
   float* logits;  // workspace [T][E] fp32
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
 };
-hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, float* wf, hipStream_t stream);
+hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, uint16_t* wt, hipStream_t stream);
 hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream);
 hipError_t launch_decode_gemv(const GemmArgs& g, bool gate_up, hipStream_t stream);
 

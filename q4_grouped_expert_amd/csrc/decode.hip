@@ -9,26 +9,31 @@
 // gfx950 mapping
 //  * Router: no candidate filter.  One wave per (token, 64 experts), one
 //    lane per expert, each lane the exact sequential fp32 chain over the
-//    hidden axis.  The router matrix is kept, once per model, as an fp32
-//    piece-major copy wf[h/4][e][4], so the 64 lanes read 1 KB of
-//    consecutive memory per step and need no bf16 unpack: four fma per
-//    16-byte load, the pieces streamed 32 ahead in registers.  The token
-//    row sits in LDS as fp32 and is read a group of pieces at a time.
+//    hidden axis.  The router matrix is kept, once per model, as a bf16
+//    piece-major copy wt[h/8][e][8], so the 64 lanes read 1 KB of
+//    consecutive memory per step: eight fma per 16-byte load, the pieces
+//    streamed 32 ahead in registers.  Each piece is unpacked to fp32 while
+//    the previous piece's fma run (a dependent fma waits about 11 clocks on
+//    gfx950; the unpacks fill those gaps).  The token row sits in LDS as fp32
+//    and is read three pieces ahead.
 //  * Top-k and grouping: one workgroup.  Wave t selects token t's experts by
 //    K rounds of a wave-wide maximum over (logit, lower expert) keys and
 //    forms the weights; then the workgroup builds counts, offsets, the stable
 //    permutation and the block map (one tile per expert with rows, then the
 //    shared expert) from the at most 256 (token, slot) pairs.
-//  * Expert GEMVs: a workgroup of 8 waves owns one tile (<= 16 rows of one
-//    expert) and 16 weight rows (gate/up: 16 gate rows and the matching 16
+//  * Expert GEMVs: a workgroup of 4 waves owns one tile (<= 16 rows of one
+//    expert) and 32 weight rows (gate/up: 16 gate rows and the matching 16
 //    up rows; down: 32 output columns as two subtiles) and splits the
-//    reduction into 8 contiguous ranges of 64-column quant groups, one per
-//    wave.  Each wave dequantizes its part of the weights (fma(q, s, b) in
-//    fp32, rounded to bf16) as the A operand of v_mfma_f32_16x16x32_bf16
-//    with the tile's activation rows as the B operand; all of a wave's loads
-//    are issued before the first MFMA.  The 8 partial 16x16 results are
-//    added in wave order through LDS, so the result does not depend on
-//    timing.
+//    reduction into 4 contiguous ranges of 64-column quant groups, one per
+//    wave.  The work is a few MB spread over the whole chip, so the limit is
+//    the number of memory requests, not bytes: each wave fetches its codes
+//    as whole 128-byte row segments straight into LDS (8 lanes per segment),
+//    the tile's scales and biases arrive as one 1 KB copy per table half,
+//    and every load of the workgroup is in flight before the first wait.
+//    Each wave dequantizes its codes (fma(q, s, b) in fp32, rounded to bf16)
+//    as the A operand of v_mfma_f32_16x16x32_bf16 with the tile's activation
+//    rows as the B operand.  The 4 partial 16x16 results are added in wave
+//    order through LDS, so the result does not depend on timing.
 //  * Combine: the prefill combine kernel.
 #include <math.h>
 
@@ -42,9 +47,10 @@ namespace moeq4 {
 namespace {
 using namespace gemm;
 
-constexpr int kDecWaves = 8;
-constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecMaxGroupsPerWave = MOE_MAX_REDUCTION / 64 / kDecWaves;  // 4
+constexpr int kGvWaves = 4;
+constexpr int kGvThreads = 64 * kGvWaves;
+constexpr int kGvMaxGroups = MOE_MAX_REDUCTION / 64 / kGvWaves;  // quant groups per wave: 8
+constexpr int kGvSegs = kGvMaxGroups * 32 / 128;                 // 128-byte code segments per row and wave: 2
 
 // Maximum of v over the 64 lanes of the wave, returned to every lane: DPP
 // row shifts build each row's maximum in its lane 15, two row broadcasts
@@ -72,17 +78,34 @@ __device__ __forceinline__ uint32_t dec_fkey(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// wf[p][e][0..3] = Wr[e][4p .. 4p+3] as fp32 (p < H/4).  One wave per expert.
+// wt[p][e][0..7] = Wr[e][8p .. 8p+7] (p < H/8).  One wave per expert.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void decode_prep_kernel(const uint16_t* __restrict__ wr, int H, int E,
-                                                         float* __restrict__ wf) {
+                                                         uint16_t* __restrict__ wt) {
   const int e = blockIdx.x;
-  for (int p = threadIdx.x; p < H / 4; p += 64) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(wr + (size_t)e * H + 4 * p);
-    const float4 f{bf16_bits_to_f32(v[0] & 0xFFFFu), bf16_bits_to_f32(v[0] >> 16), bf16_bits_to_f32(v[1] & 0xFFFFu),
-                   bf16_bits_to_f32(v[1] >> 16)};
-    *reinterpret_cast<float4*>(wf + ((size_t)p * E + e) * 4) = f;
-  }
+  for (int p = threadIdx.x; p < H / 8; p += 64)
+    *reinterpret_cast<u32x4*>(wt + ((size_t)p * E + e) * 8) = *reinterpret_cast<const u32x4*>(wr + (size_t)e * H + 8 * p);
+}
+
+// acc <- fma(x[q], u[q], acc) for q = 0..3 in order (u: fp32 weights), while
+// the four bf16 weights packed in w0, w1 are unpacked into n.  The unpacks do
+// not depend on acc and issue in the gaps between the dependent fma; one asm
+// block keeps that interleaving.
+__device__ __forceinline__ float chain4_unpack(float acc, float4 x, float u0, float u1, float u2, float u3,
+                                               uint32_t w0, uint32_t w1, float& n0, float& n1, float& n2,
+                                               float& n3) {
+  asm("v_fmac_f32 %[acc], %[xa], %[u0]\n\t"
+      "v_lshlrev_b32 %[n0], 16, %[w0]\n\t"
+      "v_fmac_f32 %[acc], %[xb], %[u1]\n\t"
+      "v_and_b32 %[n1], 0xffff0000, %[w0]\n\t"
+      "v_fmac_f32 %[acc], %[xc], %[u2]\n\t"
+      "v_lshlrev_b32 %[n2], 16, %[w1]\n\t"
+      "v_fmac_f32 %[acc], %[xd], %[u3]\n\t"
+      "v_and_b32 %[n3], 0xffff0000, %[w1]"
+      : [acc] "+v"(acc), [n0] "=&v"(n0), [n1] "=&v"(n1), [n2] "=&v"(n2), [n3] "=&v"(n3)
+      : [xa] "v"(x.x), [xb] "v"(x.y), [xc] "v"(x.z), [xd] "v"(x.w), [u0] "v"(u0), [u1] "v"(u1), [u2] "v"(u2),
+        [u3] "v"(u3), [w0] "v"(w0), [w1] "v"(w1));
+  return acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -90,15 +113,84 @@ __global__ __launch_bounds__(64) void decode_prep_kernel(const uint16_t* __restr
 // in ascending order, then + bias.  Lanes past E run a copy of expert E-1's
 // chain (every load stays in range) and store nothing.
 // ---------------------------------------------------------------------------
+template <int P>
+__device__ __forceinline__ float logit_chain(rsrc_t w_rs, uint32_t voff, uint32_t pstride, int npc, const float* xf) {
+  // Ring of P packed pieces: slot q % P holds piece q.  Piece q + 1 is
+  // unpacked while piece q runs its fma, and its slot is then reloaded with
+  // piece q + 1 + P.  Buffer loads count against the vector-memory counter
+  // only (a generic pointer load would also count against the LDS counter, so
+  // every read of the token row would wait for all loads in flight).  A
+  // single wave issues one instruction every few clocks, so the loop keeps
+  // its per-piece bookkeeping to a minimum: only the last block of P pieces
+  // clamps its load offsets to the last piece, and the token row carries
+  // three zero pieces after its end for the reads ahead.
+  u32x4 wb[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    wb[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, voff, (uint32_t)min(i, npc - 1) * pstride, 0));
+    __builtin_amdgcn_sched_barrier(0);  // keep every load at its place: P in flight
+  }
+  float u[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u[2 * k] = __uint_as_float(wb[0][k] << 16);
+    u[2 * k + 1] = __uint_as_float(wb[0][k] & 0xFFFF0000u);
+  }
+  uint32_t vo = voff;
+  wb[0] = __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, vo, (uint32_t)min(P, npc - 1) * pstride, 0));
+  // the token row of piece q in slot q % 4, read three pieces ahead (an LDS
+  // read takes longer than one piece's fma)
+  float4 xr[4][2];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    xr[k][0] = *reinterpret_cast<const float4*>(&xf[8 * k]);
+    xr[k][1] = *reinterpret_cast<const float4*>(&xf[8 * k + 4]);
+  }
+  float acc = 0.0f;
+  // one block of P pieces from p0; kLast: the block whose reloads would pass
+  // the last piece
+  auto block = [&](auto last, int p0) {
+    constexpr bool kLast = decltype(last)::value;
+    const float* xb = xf + 8 * (p0 + 3);
+    const uint32_t sbase = (uint32_t)(p0 + 1 + P) * pstride;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      xr[(i + 3) % 4][0] = *reinterpret_cast<const float4*>(xb + 8 * i);
+      xr[(i + 3) % 4][1] = *reinterpret_cast<const float4*>(xb + 8 * i + 4);
+      __builtin_amdgcn_sched_barrier(0);  // the reads go out before this piece's fma
+      const u32x4 w = wb[(i + 1) % P];
+      float n[8];
+      acc = chain4_unpack(acc, xr[i % 4][0], u[0], u[1], u[2], u[3], w[0], w[1], n[0], n[1], n[2], n[3]);
+      acc = chain4_unpack(acc, xr[i % 4][1], u[4], u[5], u[6], u[7], w[2], w[3], n[4], n[5], n[6], n[7]);
+      // reload the slot just unpacked only now (the empty asm ties the
+      // offset to acc, so the load cannot be hoisted into a second register
+      // set)
+      asm("" : "+v"(vo) : "v"(acc));
+      const uint32_t soff = kLast ? (uint32_t)min(p0 + i + 1 + P, npc - 1) * pstride : sbase + (uint32_t)i * pstride;
+      wb[(i + 1) % P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, vo, soff, 0));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) u[k] = n[k];
+    }
+  };
+  int p0 = 0;
+  for (; p0 + P < npc; p0 += P) block(std::false_type{}, p0);
+  block(std::true_type{}, p0);
+  return acc;
+}
+
 __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wf,
+                                                           const uint16_t* __restrict__ wt,
                                                            const float* __restrict__ rb, int H, int E,
                                                            float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float xf[MOE_MAX_REDUCTION];
+  // the token row as fp32, then three zero pieces (read ahead past the end)
+  __shared__ __attribute__((aligned(16))) float xf[MOE_MAX_REDUCTION + 24];
   const int neb = (E + 63) / 64;
   const int t = blockIdx.x / neb, eb = blockIdx.x - t * neb;
   const int lane = threadIdx.x;
   const int e = eb * 64 + lane;
+  if (lane < 24) xf[H + lane] = 0.0f;
   for (int h = 8 * lane; h < H; h += 512) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h);
     float4* dst = reinterpret_cast<float4*>(&xf[h]);
@@ -108,55 +200,14 @@ __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __res
                     bf16_bits_to_f32(v[3] >> 16)};
   }
   __syncthreads();
-  // Router pieces of 4 columns (np = H/4, a multiple of 16) stream P ahead in
-  // registers (32 when np allows, else 16).  The chain is bound by the
-  // latency of 2048 dependent fma (measured about 14 clocks each on gfx950,
-  // with nothing independent to issue between them); deeper prefetch does
-  // not shorten it.  The last group re-reads itself so the loop has no
-  // conditions.  The token row sits in LDS as fp32
-  // (the same address for every lane: a broadcast read), 16 pieces of it
-  // read ahead of their fma.  bf16 x bf16 products are exact in fp32, so each fma rounds
-  // exactly like acc = acc + x*w.
-  const int np = H / 4;
+  // bf16 x bf16 products are exact in fp32, so each fma rounds exactly like
+  // acc = acc + x*w
+  const int npc = H / 8;  // pieces, a multiple of 8
   const int ec = e < E ? e : E - 1;
-  const float* col = wf + (size_t)ec * 4;
-  const size_t pstride = (size_t)E * 4;
-  auto chain = [&](auto depth) {
-    constexpr int P = decltype(depth)::value;
-    float4 wb[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      wb[i] = *reinterpret_cast<const float4*>(col + i * pstride);
-      __builtin_amdgcn_sched_barrier(0);  // keep every load at its place: P in flight
-    }
-    float acc = 0.0f;
-    for (int p0 = 0; p0 < np; p0 += P) {
-      const int nxt = p0 + P < np ? p0 + P : p0;
-      float4 xv[16];
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        if (i % 16 == 0) {
-          // the token row for the next 16 pieces, read before their first fma
-#pragma unroll
-          for (int u = 0; u < 16; ++u) xv[u] = *reinterpret_cast<const float4*>(&xf[4 * (p0 + i + u)]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        acc = __builtin_fmaf(xv[i % 16].x, wb[i].x, acc);
-        acc = __builtin_fmaf(xv[i % 16].y, wb[i].y, acc);
-        acc = __builtin_fmaf(xv[i % 16].z, wb[i].z, acc);
-        acc = __builtin_fmaf(xv[i % 16].w, wb[i].w, acc);
-        // reload wb[i] only after its last use (the empty asm ties the
-        // address to acc, so the load cannot be hoisted into a second
-        // register set)
-        const float* src = col + (size_t)(nxt + i) * pstride;
-        asm("" : "+v"(src) : "v"(acc));
-        wb[i] = *reinterpret_cast<const float4*>(src);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    return acc;
-  };
-  const float acc = np % 32 == 0 ? chain(std::integral_constant<int, 32>{}) : chain(std::integral_constant<int, 16>{});
+  const rsrc_t w_rs = make_rsrc(wt, (uint32_t)E * (uint32_t)H * 2u);
+  const uint32_t voff = (uint32_t)ec * 16u, pstride = (uint32_t)E * 16u;  // bytes
+  const float acc = npc % 32 == 0 ? logit_chain<32>(w_rs, voff, pstride, npc, xf)
+                                  : logit_chain<8>(w_rs, voff, pstride, npc, xf);
   if (e < E) logits[(size_t)t * E + e] = rb ? acc + rb[e] : acc;
 }
 
@@ -296,19 +347,32 @@ __global__ __launch_bounds__(1024) void decode_group_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Split-reduction GEMV of one tile (<= 16 rows) against 16 weight rows per
-// subtile (two subtiles), see the header comment.
+// Split-reduction GEMV of one tile (<= 16 rows) against 32 weight rows, see
+// the header comment.
 // ---------------------------------------------------------------------------
+struct GemvLds {
+  // codes of each wave: [segment * 4 + row block][row in block][16-byte chunk]
+  uint8_t cl[kGvWaves][kGvSegs * 4][1024];
+  uint16_t ssh[32 * kMaxGroupsPerRow];  // [32 rows][gpr] scales
+  uint16_t bsh[32 * kMaxGroupsPerRow];  // and biases
+  f32x4 part[kGvWaves][2][64];
+};
+
 template <bool kGateUp>
-__global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) f32x4 part[kDecWaves][2][64];
+__device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
+  auto& cl = sm.cl;
+  auto& ssh = sm.ssh;
+  auto& bsh = sm.bsh;
+  auto& part = sm.part;
   const int nslice = kGateUp ? g.I / 16 : g.N / 32;
   const int tile = blockIdx.x / nslice, sl = blockIdx.x - tile * nslice;
   if (kGateUp) zero_share(g);
-  // the block-map entry is read together with n_tiles (entries past n_tiles
-  // lie inside the map and are not used)
+  // The block-map entry and the tile count arrive after one memory latency:
+  // the exit test reads both (entries past n_tiles lie inside the map; every
+  // live entry has rows), so neither load waits for the other.
   const int4 bm = *reinterpret_cast<const int4*>(g.block_map + 4 * tile);
-  if (tile >= *g.n_tiles) return;
+  const int nt = *g.n_tiles;
+  if (tile >= nt || bm.z <= 0) return;
   const int e = bm.x, row0 = bm.y, nrows = bm.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,76 +397,101 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(GemmArgs g) {
   const uint32_t a_rows = kGateUp ? (uint32_t)g.T : (uint32_t)(g.R + g.T);
   const rsrc_t a_rs = make_rsrc(g.a, a_rows * (uint32_t)Kd * 2u);
 
-  // weight rows of this lane (subtile j): gate/up: gate row 16 sl + ln and up
-  // row I + 16 sl + ln; down: output columns 32 sl + 16 j + ln
-  uint32_t wrow[2];
-  if (kGateUp) {
-    wrow[0] = (uint32_t)(16 * sl + ln);
-    wrow[1] = (uint32_t)(g.I + 16 * sl + ln);
-  } else {
-    wrow[0] = (uint32_t)(32 * sl + ln);
-    wrow[1] = (uint32_t)(32 * sl + 16 + ln);
+  // Weight row r (0..31) of the slice: gate/up: gate rows 16 sl + r for
+  // r < 16, the matching up rows I + 16 sl + r - 16 after them; down: output
+  // columns 32 sl + r.  Rows 0..15 and 16..31 are each contiguous.
+  auto wrow_of = [&](int r) -> uint32_t {
+    if (kGateUp) return (uint32_t)((r < 16 ? 0 : g.I - 16) + 16 * sl + r);
+    return (uint32_t)(32 * sl + r);
+  };
+  // tile row ln's activation row (gate/up: its token, through sorted_idx;
+  // down: h row row0 + ln); loaded first, so waiting for it leaves the DMAs
+  // issued after it in flight
+  const bool arow = ln < nrows;
+  int sidx = 0;
+  if (kGateUp && arow && row0 + ln < g.R) sidx = g.sorted_idx[row0 + ln];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the tile's scale and bias tables ([32 rows][gpr] each): wave w
+  // copies half w & 1 (16 rows, 32 gpr bytes <= 1 KB) of table w >> 1; only
+  // the lanes inside the half copy (the two halves' LDS ranges are adjacent)
+  {
+    const int half = wave & 1;
+    const uint32_t bytes = 32u * (uint32_t)gpr;
+    uint16_t* dst = (wave < 2 ? ssh : bsh) + half * 16 * gpr;
+    if (16u * lane < bytes)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? s_rs : b_rs, (__attribute__((address_space(3))) void*)dst,
+                                               16, wrow_of(16 * half) * (uint32_t)gpr * 2u + 16u * lane, 0, 0, 0);
   }
-  // activation column ln of the MFMA: row ln of the tile (gate/up: its
-  // token's x row; down: h row row0 + ln); columns past the tile read zeros
+  // ---- this wave's codes: quant groups [g0, g1) (at most kGvMaxGroups), as
+  // whole 128-byte segments of each of the 32 rows.  DMA (s, rb) fills rows
+  // 8 rb .. 8 rb + 7 with segment s: lane l lands at row 8 rb + l/8,
+  // physical chunk l%8, and fetches logical chunk (l%8) ^ (l/8), so that the
+  // 16 rows one read touches spread over the banks.  Chunks past g1 read
+  // zeros.
+  const int g0 = (gpr * wave) / kGvWaves, g1 = (gpr * (wave + 1)) / kGvWaves;
+  const int ng = g1 - g0;
+  {
+    const int r8 = lane >> 3;
+    const int c = (lane & 7) ^ r8;
+#pragma unroll
+    for (int sg = 0; sg < kGvSegs; ++sg)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const uint32_t b = 128u * sg + 16u * c;  // byte of the wave's row range
+        const uint32_t off = b < 32u * (uint32_t)ng ? wrow_of(8 * rb + r8) * cpr + 32u * g0 + b : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c_rs, (__attribute__((address_space(3))) void*)&cl[wave][sg * 4 + rb][0], 16, off, 0, 0, 0);
+      }
+  }
+  // ---- activations as the B operand: lane (ln, lg) holds tile row ln,
+  // columns 64 g + 16 lg + 8 st of group g for MFMA step st (the k order of
+  // the code word; the same permutation on both operands); rows past the
+  // tile and groups past g1 read zeros
   uint32_t aoff = kOob;
-  if (ln < nrows) {
+  if (arow) {
     const int p = row0 + ln;
-    int src;
-    if (kGateUp) src = (p < g.R) ? g.sorted_idx[p] / g.topk : p - g.R;
-    else src = p;
-    aoff = (uint32_t)src * (uint32_t)Kd * 2u;
+    const int src = kGateUp ? (p < g.R ? sidx / g.topk : p - g.R) : p;
+    aoff = (uint32_t)src * (uint32_t)Kd * 2u + 32u * lg;
   }
-  // per-lane part of the activation offsets (columns 16 lg + 8 st of a group)
-  const uint32_t aoff_l[2] = {aoff == kOob ? kOob : aoff + 32u * lg, aoff == kOob ? kOob : aoff + 32u * lg + 16u};
-  // this wave's quant groups: [g0, g1)
-  const int g0 = (gpr * wave) / kDecWaves, g1 = (gpr * (wave + 1)) / kDecWaves;
+  u32x4 av[kGvMaxGroups][2];
+#pragma unroll
+  for (int i = 0; i < kGvMaxGroups; ++i)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      av[i][st] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, i < ng ? aoff + 16u * st : kOob, (g0 + i) * 128, 0));
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave's table copy has landed
+
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (g0 < g1) {
-    u32x2 cw[kDecMaxGroupsPerWave][2];
-    uint32_t sw[kDecMaxGroupsPerWave][2], bw[kDecMaxGroupsPerWave][2];
-    u32x4 av[kDecMaxGroupsPerWave][2];
-    // every load of the wave first (at most 4 groups: gpr <= 32)
 #pragma unroll
-    for (int i = 0; i < kDecMaxGroupsPerWave; ++i) {
-      const int gi = g0 + i;
-      if (gi < g1) {
+  for (int i = 0; i < kGvMaxGroups; ++i) {
+    if (i < ng) {
+      const int sg = i / 4;
+      const int c = 2 * (i % 4) + (lg >> 1);  // logical chunk of the segment
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          cw[i][j] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(c_rs, wrow[j] * cpr + 8u * lg, gi * 32, 0));
-          sw[i][j] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, wrow[j] * (uint32_t)gpr * 2u, gi * 2, 0);
-          bw[i][j] = __builtin_amdgcn_raw_buffer_load_b16(b_rs, wrow[j] * (uint32_t)gpr * 2u, gi * 2, 0);
-        }
-        // activation columns 16 lg .. 16 lg + 15 of the group: the k order
-        // of the code word (the same permutation on both operands)
+      for (int j = 0; j < 2; ++j) {
+        const int r = 16 * j + ln;  // row of the slice
+        const int r8 = r & 7;
+        const u32x2 cw = *reinterpret_cast<const u32x2*>(&cl[wave][sg * 4 + (r >> 3)][r8 * 128 + (c ^ r8) * 16 +
+                                                                                      8 * (lg & 1)]);
+        const float sv = bf16_bits_to_f32(ssh[r * gpr + g0 + i]), bv = bf16_bits_to_f32(bsh[r * gpr + g0 + i]);
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          av[i][st] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, aoff_l[st], gi * 128, 0));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kDecMaxGroupsPerWave; ++i) {
-      if (g0 + i < g1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float s = bf16_bits_to_f32(sw[i][j] & 0xFFFFu), b = bf16_bits_to_f32(bw[i][j] & 0xFFFFu);
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            mfma_acc(acc[j], dequant8(cw[i][j][st], s, b), __builtin_bit_cast(bf16x8, av[i][st]));
-        }
+          mfma_acc(acc[j], dequant8(cw[st], sv, bv), __builtin_bit_cast(bf16x8, av[i][st]));
       }
     }
   }
   // lane holds weight rows 4 lg .. 4 lg + 3 of each subtile for tile row ln;
-  // the partials of the 8 waves are added in wave order
+  // the partials of the 4 waves are added in wave order
   part[wave][0][lane] = acc[0];
   part[wave][1][lane] = acc[1];
   __syncthreads();
   if (wave != 0 || ln >= nrows) return;
   f32x4 s0 = part[0][0][lane], s1 = part[0][1][lane];
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) {
+  for (int w = 1; w < kGvWaves; ++w) {
     s0 += part[w][0][lane];
     s1 += part[w][1][lane];
   }
@@ -428,16 +517,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(GemmArgs g) {
   }
 }
 
+template <bool kGateUp>
+__global__ __launch_bounds__(kGvThreads) void decode_gemv_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) GemvLds sm;
+  gemv_body<kGateUp>(g, sm);
+}
+
 }  // namespace
 
-hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, float* wf, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(E), dim3(64), 0, stream, wr, H, E, wf);
+hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, uint16_t* wt, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(E), dim3(64), 0, stream, wr, H, E, wt);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream) {
   const int neb = (a.E + 63) / 64;
-  hipLaunchKernelGGL(decode_logits_kernel, dim3(a.T * neb), dim3(64), 0, stream, a.x, a.wf, a.router_bias, a.H, a.E,
+  hipLaunchKernelGGL(decode_logits_kernel, dim3(a.T * neb), dim3(64), 0, stream, a.x, a.wt, a.router_bias, a.H, a.E,
                      a.logits);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -449,9 +544,9 @@ hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream) {
 hipError_t launch_decode_gemv(const GemmArgs& g, bool gate_up, hipStream_t stream) {
   const int nslice = gate_up ? g.I / 16 : g.N / 32;
   if (gate_up)
-    hipLaunchKernelGGL(decode_gemv_kernel<true>, dim3(g.max_tiles * nslice), dim3(kDecThreads), 0, stream, g);
+    hipLaunchKernelGGL(decode_gemv_kernel<true>, dim3(g.max_tiles * nslice), dim3(kGvThreads), 0, stream, g);
   else
-    hipLaunchKernelGGL(decode_gemv_kernel<false>, dim3(g.max_tiles * nslice), dim3(kDecThreads), 0, stream, g);
+    hipLaunchKernelGGL(decode_gemv_kernel<false>, dim3(g.max_tiles * nslice), dim3(kGvThreads), 0, stream, g);
   return hipGetLastError();
 }
 

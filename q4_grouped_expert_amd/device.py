@@ -87,12 +87,12 @@ class DeviceLayer:
                                    stream)
 
     def decode_router(self) -> torch.Tensor:
-        """The fp32 piece-major router copy the decode path reads (made once)."""
-        if getattr(self, "_wf", None) is None:
+        """The bf16 piece-major router copy the decode path reads (made once)."""
+        if getattr(self, "_wt", None) is None:
             s = self.shape
-            self._wf = torch.empty((s.H // 4, s.E, 4), dtype=torch.float32, device=self.device)
-            B.moe_decode_router_prepare(self.desc(0), self.w_router, self._wf)
-        return self._wf
+            self._wt = torch.empty((s.H // 8, s.E, 8), dtype=torch.int16, device=self.device)
+            B.moe_decode_router_prepare(self.desc(0), self.w_router, self._wt)
+        return self._wt
 
     def decode(self, x: torch.Tensor, out: torch.Tensor, route: Optional[dict] = None, stream=None):
         """The decode-shape layer for at most 16 tokens."""
