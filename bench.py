@@ -239,7 +239,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; the GPU takes some tens of milliseconds of load to reach its steady clock")
     ap.add_argument("--workload", default="prefill4096",
                     help="prefill4096 (default), prefill512, skew2048, long16384, tiny; decode1, decode4, "
                          "decode16 (decode-shape layer); gdn4096, gdn512, gdn_tiny (Gated DeltaNet prefill scan); "

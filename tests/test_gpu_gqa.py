@@ -45,6 +45,7 @@ def assert_close(got, ref, what="out"):
     err = np.abs(got.astype(np.float64) - ref)
     mx = err.max() / max(np.abs(ref).max(), 1e-30)
     mean = err.sum() / max(np.abs(ref).sum(), 1e-30)
+    print(f"   {what}: max_rel={mx:.3e} mean_rel={mean:.3e}", flush=True)
     assert mx <= TOL_MAX and mean <= TOL_MEAN, f"{what}: max_rel={mx:.3e} mean_rel={mean:.3e}"
 
 
