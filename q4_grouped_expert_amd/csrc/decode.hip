@@ -180,18 +180,12 @@ __device__ __forceinline__ float logit_chain(rsrc_t w_rs, uint32_t voff, uint32_
   return acc;
 }
 
-__global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wt,
-                                                           const float* __restrict__ rb, int H, int E,
-                                                           float* __restrict__ logits) {
-  // the token row as fp32, then three zero pieces (read ahead past the end)
-  __shared__ __attribute__((aligned(16))) float xf[MOE_MAX_REDUCTION + 24];
-  const int neb = (E + 63) / 64;
-  const int t = blockIdx.x / neb, eb = blockIdx.x - t * neb;
-  const int lane = threadIdx.x;
-  const int e = eb * 64 + lane;
-  if (lane < 24) xf[H + lane] = 0.0f;
-  for (int h = 8 * lane; h < H; h += 512) {
+// Token t's row of x into LDS as fp32, then three zero pieces (read ahead
+// past the end), by the threads [first, first + n).
+__device__ __forceinline__ void token_row_to_lds(const uint16_t* __restrict__ x, int t, int H, float* xf, int i,
+                                                 int n) {
+  if (i < 24) xf[H + i] = 0.0f;
+  for (int h = 8 * i; h < H; h += 8 * n) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h);
     float4* dst = reinterpret_cast<float4*>(&xf[h]);
     dst[0] = float4{bf16_bits_to_f32(v[0] & 0xFFFFu), bf16_bits_to_f32(v[0] >> 16), bf16_bits_to_f32(v[1] & 0xFFFFu),
@@ -199,16 +193,36 @@ __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __res
     dst[1] = float4{bf16_bits_to_f32(v[2] & 0xFFFFu), bf16_bits_to_f32(v[2] >> 16), bf16_bits_to_f32(v[3] & 0xFFFFu),
                     bf16_bits_to_f32(v[3] >> 16)};
   }
-  __syncthreads();
-  // bf16 x bf16 products are exact in fp32, so each fma rounds exactly like
-  // acc = acc + x*w
+}
+
+// The logit of expert e (this lane) against the token row xf: the exact
+// chain, then + bias.  Lanes past E run a copy of expert E-1's chain (every
+// load stays in range); the caller stores nothing for them.  bf16 x bf16
+// products are exact in fp32, so each fma rounds exactly like acc = acc + x*w.
+__device__ __forceinline__ float lane_logit(const uint16_t* __restrict__ wt, const float* __restrict__ rb, int H,
+                                           int E, int e, const float* xf) {
   const int npc = H / 8;  // pieces, a multiple of 8
   const int ec = e < E ? e : E - 1;
   const rsrc_t w_rs = make_rsrc(wt, (uint32_t)E * (uint32_t)H * 2u);
   const uint32_t voff = (uint32_t)ec * 16u, pstride = (uint32_t)E * 16u;  // bytes
   const float acc = npc % 32 == 0 ? logit_chain<32>(w_rs, voff, pstride, npc, xf)
                                   : logit_chain<8>(w_rs, voff, pstride, npc, xf);
-  if (e < E) logits[(size_t)t * E + e] = rb ? acc + rb[e] : acc;
+  return rb && e < E ? acc + rb[e] : acc;
+}
+
+__global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wt,
+                                                           const float* __restrict__ rb, int H, int E,
+                                                           float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float xf[MOE_MAX_REDUCTION + 24];
+  const int neb = (E + 63) / 64;
+  const int t = blockIdx.x / neb, eb = blockIdx.x - t * neb;
+  const int lane = threadIdx.x;
+  const int e = eb * 64 + lane;
+  token_row_to_lds(x, t, H, xf, lane, 64);
+  __syncthreads();
+  const float l = lane_logit(wt, rb, H, E, e, xf);
+  if (e < E) logits[(size_t)t * E + e] = l;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,11 +237,19 @@ __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __res
 // counts, offsets, stable sorted_idx / inv_pos, the block map (one tile per
 // expert with rows, in expert order, then the shared expert's) and n_tiles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void decode_group_kernel(const float* __restrict__ logits, int T, int K, int E,
-                                                            int norm_topk, int has_shared, moe_route_out out) {
-  __shared__ int sid[MOE_MAX_EXPERTS];
-  __shared__ int wsum[MOE_MAX_EXPERTS / 64][2];
-  __shared__ int off_s[MOE_MAX_EXPERTS];
+struct GroupLds {
+  int sid[MOE_MAX_EXPERTS];
+  int wsum[MOE_MAX_EXPERTS / 64][2];
+  int off_s[MOE_MAX_EXPERTS];
+};
+
+// Called by every thread of a workgroup of at least max(T, 4) waves; logits
+// [T][E] in global memory or LDS, complete and visible to the workgroup.
+__device__ __forceinline__ void group_body(const float* logits, int T, int K, int E, int norm_topk, int has_shared,
+                                           const moe_route_out& out, GroupLds& sm) {
+  auto& sid = sm.sid;
+  auto& wsum = sm.wsum;
+  auto& off_s = sm.off_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (wave < T) {
@@ -344,6 +366,46 @@ __global__ __launch_bounds__(1024) void decode_group_kernel(const float* __restr
     out.sorted_idx[p] = tid;
     out.inv_pos[tid] = p;
   }
+}
+
+__global__ __launch_bounds__(1024) void decode_group_kernel(const float* __restrict__ logits, int T, int K, int E,
+                                                            int norm_topk, int has_shared, moe_route_out out) {
+  __shared__ GroupLds sm;
+  group_body(logits, T, K, E, norm_topk, has_shared, out, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Router and grouping in one workgroup for at most kDecFusedTokens tokens:
+// wave w computes the logits of token w / neb, experts 64 (w % neb) ..
+// (every chain on its own wave, as in the two-kernel form), into LDS; then
+// the workgroup runs the grouping above.  One launch fewer.
+// ---------------------------------------------------------------------------
+constexpr int kDecFusedTokens = 2;  // 8 waves at most: 256 registers per lane for the chain
+
+__global__ __launch_bounds__(512) void decode_route_fused_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wt,
+                                                                  const float* __restrict__ rb, int T, int H, int E,
+                                                                  int K, int norm_topk, int has_shared,
+                                                                  moe_route_out out) {
+  __shared__ __attribute__((aligned(16))) float xf[kDecFusedTokens][MOE_MAX_REDUCTION + 24];
+  __shared__ float lg[kDecFusedTokens * MOE_MAX_EXPERTS];
+  __shared__ GroupLds sm;
+  const int neb = (E + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = blockDim.x >> 6;
+  // token rows: the waves share them out, token t to waves t, t + T, ...
+  for (int t = 0; t < T; ++t)
+    if (wave % T == t) token_row_to_lds(x, t, H, xf[t], tid - 64 * wave + 64 * (wave / T), 64 * ((nw - t + T - 1) / T));
+  __syncthreads();
+  if (wave < T * neb) {
+    const int t = wave / neb, eb = wave - t * neb;
+    const int e = eb * 64 + lane;
+    const float l = lane_logit(wt, rb, H, E, e, xf[t]);
+    if (e < E) lg[t * E + e] = l;
+  }
+  __syncthreads();
+  group_body(lg, T, K, E, norm_topk, has_shared, out, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -532,6 +594,12 @@ hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, uint16_t* wt, hi
 
 hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream) {
   const int neb = (a.E + 63) / 64;
+  if (a.T <= kDecFusedTokens) {
+    const int waves = a.T * neb > 4 ? a.T * neb : 4;  // the grouping needs 256 threads
+    hipLaunchKernelGGL(decode_route_fused_kernel, dim3(1), dim3(64 * waves), 0, stream, a.x, a.wt, a.router_bias, a.T,
+                       a.H, a.E, a.K, a.norm_topk, a.has_shared, a.out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(decode_logits_kernel, dim3(a.T * neb), dim3(64), 0, stream, a.x, a.wt, a.router_bias, a.H, a.E,
                      a.logits);
   hipError_t err = hipGetLastError();
