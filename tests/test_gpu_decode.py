@@ -3,8 +3,9 @@ tokens) against the CPU oracle on the same seeded inputs: routing (ids,
 counts, offsets, permutation, block map) bit-exact, weights to 2e-6, layer
 outputs within max|err| <= 2e-2 max|ref| and sum|err|/sum|ref| <= 5e-3.
 The prefill path on the same tokens must give the same routing bit for bit.
-Single-token cases run the expert FFN as split-reduction GEMVs, the others
-as the tiled grouped GEMM."""
+Up to 4 tokens the expert FFN runs as split-reduction GEMVs, from 5 tokens
+as the tiled grouped GEMM; up to 2 tokens the router and the grouping run in
+one workgroup."""
 
 import numpy as np
 import pytest
@@ -38,6 +39,12 @@ CASES = {
     "T1_H64_I64": gen.custom_shape(1, 64, 64, 8, 2, seed=77),
     "T1_H2048_I2048": gen.custom_shape(1, 2048, 2048, 8, 2, seed=78),
     "T1_k_eq_E": gen.custom_shape(1, 256, 128, 16, 16, seed=79),
+    # 2 and 4 tokens at full size (one-workgroup routing, GEMVs); expert
+    # counts that are not multiples of 64 (a partial last wave of logits)
+    "T2_full": gen.custom_shape(2, 2048, 512, 256, 8, seed=80),
+    "T4_full": gen.custom_shape(4, 2048, 512, 256, 8, seed=81),
+    "T2_E100_K6": gen.custom_shape(2, 256, 128, 100, 6, seed=82),
+    "T1_E200": gen.custom_shape(1, 512, 256, 200, 8, seed=83),
 }
 
 
