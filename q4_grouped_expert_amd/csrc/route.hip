@@ -359,7 +359,12 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
   // the step are issued before any is used
   float av[TPW][4];
   {
+    // this lane's four experts' partial sums, one 16-byte load per split and
+    // token (experts past E read what follows in the array, or zeros past
+    // its end, and are masked below)
+    const rsrc_t a_rs = rsrc_of(alog, (uint32_t)NSPLIT * T * E * 4u);
     u32x4 v[TPW][NP];
+    u32x4 pa[TPW][NSPLIT];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = t0 + TPW * wave + j;
@@ -369,27 +374,23 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
         const uint32_t off = t < T && h < H ? ((uint32_t)t * H + h) * 2u : kOob;
         v[j][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
       }
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) {
+        const uint32_t off = t < T && 4 * lane < E ? (((uint32_t)sp * T + t) * E + 4 * lane) * 4u : kOob;
+        pa[j][sp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, off, 0, 0));
+      }
     }
     // the approximate logits: the hidden-axis splits added in order (the
     // bias follows in the candidate step)
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      const int t = t0 + TPW * wave + j;
+      const bool tv = t0 + TPW * wave + j < T;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int e = 4 * lane + q;
-        float v = 0.0f;
-        if (t < T && e < E) {
-          // every split's load is issued before the adds, then the partial
-          // sums are added in split order
-          float pv[NSPLIT];
+        float v = __uint_as_float(pa[j][0][q]);
 #pragma unroll
-          for (int sp = 0; sp < NSPLIT; ++sp) pv[sp] = alog[((size_t)sp * T + t) * E + e];
-          v = pv[0];
-#pragma unroll
-          for (int sp = 1; sp < NSPLIT; ++sp) v += pv[sp];
-        }
-        av[j][q] = v;
+        for (int sp = 1; sp < NSPLIT; ++sp) v += __uint_as_float(pa[j][sp][q]);
+        av[j][q] = tv && 4 * lane + q < E ? v : 0.0f;
       }
     }
     float wv[MOE_MAX_EXPERTS / 64];
