@@ -108,6 +108,26 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 __device__ __forceinline__ float fkey_inv(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
+// Sum over the 64 lanes, every lane getting the total, in a fixed order that
+// only the norms' bound relies on: DPP within rows of 16, then the row-pair
+// and half-wave swaps (with both operands the same register, a swap leaves a
+// block's value in one output and its neighbour's in the other).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float a) {
+  a = a + dpp_f32<0xB1>(a);   // quad_perm [1,0,3,2]
+  a = a + dpp_f32<0x4E>(a);   // quad_perm [2,3,0,1]
+  a = a + dpp_f32<0x141>(a);  // row_half_mirror
+  a = a + dpp_f32<0x140>(a);  // row_mirror
+  const uint32_t u = __float_as_uint(a);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const uint32_t w = __float_as_uint(a);
+  const auto h = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
 // Lanes below this one in the wave.
 __device__ __forceinline__ uint64_t lanes_below() {
   return (1ull << __lane_id()) - 1ull;
@@ -420,8 +440,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
           dst[1] = float4{f[4], f[5], f[6], f[7]};
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+      s2 = wave_sum_f32(s2);
       if (lane == 0) xn_s[tk] = sqrtf(s2);
     }
     if (wave == 0) {
