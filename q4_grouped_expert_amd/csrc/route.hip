@@ -89,6 +89,7 @@ __device__ __forceinline__ int rswz(int row, int c) { return c ^ (row & 7) ^ ((r
 constexpr int kLgTile = 64;  // tokens and experts per approximate-logits workgroup
 constexpr int kMaxLogitSplits = 8;  // hidden-axis splits of the approximate logits
 constexpr int kLgK = 64;     // hidden columns per stage
+constexpr int kLgRing = 4;   // LDS ring slots (loads run kLgRing - 1 stages ahead)
 // s_waitcnt that bounds only the vector-memory counter (gfx9 encoding: vmcnt
 // in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
@@ -140,8 +141,8 @@ __device__ __forceinline__ uint64_t lanes_below() {
 //
 // One workgroup: 64 tokens x 64 experts; wave w owns the 32 x 32 quadrant
 // (tokens 32 (w & 1).., experts 32 (w >> 1)..) as 2 x 2 MFMA tiles.  Token
-// and router rows stream through a 3-slot LDS ring of 64-column stages
-// filled by direct-to-LDS loads two stages ahead.  Every MFMA adds a
+// and router rows stream through a 4-slot LDS ring of 64-column stages
+// filled by direct-to-LDS loads three stages ahead.  Every MFMA adds a
 // 32-product step to its fp32 accumulator, the structure the selection
 // kernel's error bound assumes.
 //
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb,
                                                            int hist_len) {
   constexpr int kRows = 2 * kLgTile;            // token rows, then router rows
   constexpr int kSlot = kRows * kLgK;           // bf16 elements per ring slot
-  __shared__ __attribute__((aligned(16))) uint16_t ring[3 * kSlot];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kLgRing * kSlot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // What the selection kernel (the next launch) reads besides the logits:
@@ -234,33 +235,35 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a, int ntb,
     }
   };
 
-  // Stage kt DMAs stage kt+2 into the slot read in stage kt-1 (free since
-  // the last barrier), computes on slot kt%3, then waits until only its own
-  // DMAs of this stage are in flight (so stage kt+1 has landed) and meets
-  // the other waves at the barrier.  Past the last stage the DMAs repeat
-  // the last one, keeping the count per stage fixed; no other vector-memory
-  // access runs inside the loop, so the count is exact.
+  // Stage kt DMAs stage kt + R - 1 (R = kLgRing slots) into the slot read in
+  // stage kt - 1 (free since the last barrier), computes on slot kt % R, then
+  // waits until only the DMAs of its last R - 2 stages are in flight (so
+  // stage kt + 1 has landed) and meets the other waves at the barrier.  Past
+  // the last stage the DMAs repeat the last one, keeping the count per stage
+  // fixed; no other vector-memory access runs inside the loop, so the count
+  // is exact.
+  constexpr int R = kLgRing;
   const int last = nk - 1;
-  dma(0, 0);
-  dma(1, min(1, last));
-  wait_vmcnt<kDmaPerStage>();
+#pragma unroll
+  for (int s0 = 0; s0 < R - 1; ++s0) dma(s0, min(s0, last));
+  wait_vmcnt<(R - 2) * kDmaPerStage>();
   __builtin_amdgcn_s_barrier();
   int kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
+  for (; kt + R <= nk; kt += R) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      dma((u + 2) % 3, min(kt + u + 2, last));
+    for (int u = 0; u < R; ++u) {
+      dma((u + R - 1) % R, min(kt + u + R - 1, last));
       stage(u);
-      wait_vmcnt<kDmaPerStage>();
+      wait_vmcnt<(R - 2) * kDmaPerStage>();
       __builtin_amdgcn_s_barrier();
     }
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < R - 1; ++u) {
     if (kt + u < nk) {
-      dma((u + 2) % 3, min(kt + u + 2, last));
+      dma((u + R - 1) % R, min(kt + u + R - 1, last));
       stage(u);
-      wait_vmcnt<kDmaPerStage>();
+      wait_vmcnt<(R - 2) * kDmaPerStage>();
       __builtin_amdgcn_s_barrier();
     }
   }
