@@ -53,22 +53,22 @@ constexpr int kGvMaxGroups = MOE_MAX_REDUCTION / 64 / kGvWaves;  // quant groups
 constexpr int kGvSegs = kGvMaxGroups * 32 / 128;                 // 128-byte code segments per row and wave: 2
 
 // Maximum of v over the 64 lanes of the wave, returned to every lane: DPP
-// row shifts build each row's maximum in its lane 15, two row broadcasts
-// carry them to lane 63 (the identity is 0, below every value used here).
-template <int kCtrl, int kRowMask, int kBankMask>
+// exchanges inside each row of 16 lanes, then the row-pair and half-wave
+// swaps (with both operands the same register, a swap leaves a block's
+// value in one output and its neighbour's in the other).
+template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, kBankMask, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  uint32_t r = v;
-  r = max(r, dpp_u32<0x111, 0xf, 0xf>(v));  // row_shr:1
-  r = max(r, dpp_u32<0x112, 0xf, 0xf>(v));  // row_shr:2
-  r = max(r, dpp_u32<0x113, 0xf, 0xf>(v));  // row_shr:3
-  r = max(r, dpp_u32<0x114, 0xf, 0xe>(r));  // row_shr:4, banks 1-3
-  r = max(r, dpp_u32<0x118, 0xf, 0xc>(r));  // row_shr:8, banks 2-3
-  r = max(r, dpp_u32<0x142, 0xa, 0xf>(r));  // row_bcast:15 into rows 1 and 3
-  r = max(r, dpp_u32<0x143, 0xc, 0xf>(r));  // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t a) {
+  a = max(a, dpp_u32<0xB1>(a));   // quad_perm [1,0,3,2]
+  a = max(a, dpp_u32<0x4E>(a));   // quad_perm [2,3,0,1]
+  a = max(a, dpp_u32<0x141>(a));  // row_half_mirror
+  a = max(a, dpp_u32<0x140>(a));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  a = max((uint32_t)r[0], (uint32_t)r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  return max((uint32_t)h[0], (uint32_t)h[1]);
 }
 
 // Order-preserving map of an fp32 value to uint32 (-0 taken as +0).
@@ -228,19 +228,26 @@ __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // Top-k, weights and grouping for at most 16 tokens in one workgroup.
 //
-// Wave t (token t) holds experts 4 l .. 4 l + 3 in lane l as keys
-// fkey(logit) << 8 | 255 - e (larger = larger logit, then lower expert) and
-// takes K rounds of a wave-wide maximum, each removing the winner: the
-// winners in order are the slots.  Weights: exp(l - l_max) over the sum of
-// exp(l - l_max) of the selection (norm_topk) or of every expert, the sums
-// in a fixed lane tree.  Then, for the at most 256 (token, slot) pairs:
-// counts, offsets, stable sorted_idx / inv_pos, the block map (one tile per
-// expert with rows, in expert order, then the shared expert's) and n_tiles.
+// Wave t (token t) holds experts 4 l .. 4 l + 3 in lane l as order-preserving
+// keys of their logits and takes K rounds: the wave-wide maximum key, then
+// the lowest lane holding it (a ballot) and that lane's lowest expert with
+// it, which is the lowest expert with the largest logit; the winner's key is
+// removed and the winners in order are the slots.  Weights: exp(l - l_max)
+// over the sum of exp(l - l_max) of the selection (norm_topk) or of every
+// expert, the sums in a fixed lane tree.  Then, for the at most 256
+// (token, slot) pairs, one per thread: each wave finds the lanes whose pair
+// has the same expert with eight ballots (one per bit of the expert index),
+// which gives a pair's rank among the earlier pairs of its wave and each
+// expert's count per wave; counts, offsets, the stable sorted_idx / inv_pos,
+// the block map (one tile per expert with rows, in expert order, then the
+// shared expert's) and n_tiles follow from those.
 // ---------------------------------------------------------------------------
+constexpr int kPairWaves = MOE_MAX_EXPERTS / 64;  // waves of (token, slot) pairs, R <= 256
 struct GroupLds {
   int sid[MOE_MAX_EXPERTS];
   int wsum[MOE_MAX_EXPERTS / 64][2];
   int off_s[MOE_MAX_EXPERTS];
+  int cntw[kPairWaves][MOE_MAX_EXPERTS];  // pairs of wave w with expert e
 };
 
 // Called by every thread of a workgroup of at least max(T, 4) waves; logits
@@ -252,40 +259,42 @@ __device__ __forceinline__ void group_body(const float* logits, int T, int K, in
   auto& off_s = sm.off_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // every count of a pair wave starts at zero (the waves past T are idle now)
+  for (int i = tid; i < kPairWaves * MOE_MAX_EXPERTS; i += blockDim.x) (&sm.cntw[0][0])[i] = 0;
+
   if (wave < T) {
     const int t = wave;
-    unsigned long long kq[4];
+    uint32_t kq[4];
     float lv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
       lv[q] = e < E ? logits[(size_t)t * E + e] : 0.0f;
-      kq[q] = e < E ? ((unsigned long long)dec_fkey(lv[q]) << 8) | (unsigned)(255 - e) : 0ull;
+      kq[q] = e < E ? dec_fkey(lv[q]) : 0u;  // every logit's key is above 0
     }
-    float mysel = 0.0f;  // lane k < K: the slot-k logit
+    float mysel = 0.0f;  // lane k < K: the slot-k logit and expert
+    int myid = 0;
     for (int k = 0; k < K; ++k) {
-      // the wave's largest key: largest logit key, then among the lanes that
-      // hold it the largest 255 - e (the lowest expert)
-      unsigned long long lm = kq[0];
+      const uint32_t lm = max(max(kq[0], kq[1]), max(kq[2], kq[3]));
+      const uint32_t m = wave_max_u32(lm);
+      // lane l holds experts 4l..4l+3, so the lowest lane holding the key
+      // holds the lowest expert with it
+      const int wl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lm == m));
+      const int qf = kq[0] == m ? 0 : kq[1] == m ? 1 : kq[2] == m ? 2 : 3;
+      const int qs = __builtin_amdgcn_readlane(qf, wl);
+      const float lq = qs == 0 ? lv[0] : qs == 1 ? lv[1] : qs == 2 ? lv[2] : lv[3];
+      const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lq), wl));
+      const bool mine = lane == wl;
 #pragma unroll
-      for (int q = 1; q < 4; ++q) lm = kq[q] > lm ? kq[q] : lm;
-      const uint32_t hi = wave_max_u32((uint32_t)(lm >> 8));
-      const uint32_t lo = wave_max_u32((uint32_t)(lm >> 8) == hi ? (uint32_t)(lm & 255ull) : 0u);
-      const unsigned long long m = ((unsigned long long)hi << 8) | lo;
-      const int e = 255 - (int)lo;
+      for (int q = 0; q < 4; ++q) kq[q] = (mine && q == qs) ? 0u : kq[q];  // taken
       if (lane == k) {
-        out.topk_ids[(size_t)t * K + k] = e;
-        sid[t * K + k] = e;
+        myid = 4 * wl + qs;
+        mysel = val;
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (kq[q] == m) kq[q] = 0ull;  // taken (keys are distinct)
-      // the slot-k logit, from the lane that holds expert e
-      float val = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) val = (4 * lane + q == e) ? lv[q] : val;
-      val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), e >> 2));
-      if (lane == k) mysel = val;
+    }
+    if (lane < K) {
+      out.topk_ids[(size_t)t * K + lane] = myid;
+      sid[t * K + lane] = myid;
     }
     const float mx = __shfl(mysel, 0);
     float part = 0.0f, ev = 0.0f;
@@ -304,11 +313,26 @@ __device__ __forceinline__ void group_body(const float* logits, int T, int K, in
   }
   __syncthreads();
 
-  // ---- grouping of the R = T*K pairs (threads 0..255, one per expert) ------
+  // ---- grouping of the R = T*K pairs -----------------------------------------
   const int R = T * K;  // <= 256
-  int c = 0, ne = 0;
+  int x = 0, rank = 0;  // thread i < R: pair i's expert and its rank among the wave's earlier pairs
+  if (tid < R) {
+    x = sid[tid];
+    uint64_t same = __builtin_amdgcn_ballot_w64(true);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {  // expert indices are below 256
+      const bool bit = (x >> b) & 1;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(bit);
+      same &= bit ? m : ~m;
+    }
+    rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+    if (rank == 0) sm.cntw[wave][x] = __popcll(same);
+  }
+  __syncthreads();
+  int c = 0, ne = 0;  // thread e < 256: expert e's pairs
   if (tid < MOE_MAX_EXPERTS) {
-    for (int i = 0; i < R; ++i) c += sid[i] == tid ? 1 : 0;
+#pragma unroll
+    for (int w = 0; w < kPairWaves; ++w) c += sm.cntw[w][tid];
     ne = c > 0 ? 1 : 0;
   }
   int ic = c, in = ne;  // inclusive scans of counts and of non-empty experts
@@ -359,9 +383,7 @@ __device__ __forceinline__ void group_body(const float* logits, int T, int K, in
   }
   __syncthreads();
   if (tid < R) {
-    const int x = sid[tid];
-    int rank = 0;
-    for (int i = 0; i < tid; ++i) rank += sid[i] == x ? 1 : 0;
+    for (int w = 0; w < wave; ++w) rank += sm.cntw[w][x];  // the expert's pairs in earlier waves
     const int p = off_s[x] + rank;
     out.sorted_idx[p] = tid;
     out.inv_pos[tid] = p;
