@@ -710,14 +710,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 // Group offsets, tile block map and stable scatter (sorted_idx / inv_pos).
 //
 // hist[e][g] holds the rows of expert e among the tokens of group g (64
-// tokens each); rows are ngp = ng rounded up to 4 ints long.  One workgroup per group, one thread per expert: it sums its
-// expert's row of hist into the total count and the rows that earlier groups
-// own, a workgroup-wide exclusive scan of the totals gives the expert group
-// offsets, and the first wave places the group's rows: a (t, k) row goes to
-// offsets[e] + (rows of e in earlier groups) + (earlier tokens of this group
-// that chose e, from a 64-bit LDS mask).  Workgroup 0 also writes counts,
-// offsets and the block map (each expert's tiles of at most kTileRows rows,
-// then the shared expert's).
+// tokens each); rows are ngp = ng rounded up to 4 ints long.  One workgroup
+// per group, one thread per expert: it sums its expert's row of hist into the
+// total count and the rows that earlier groups own, and a workgroup-wide
+// exclusive scan of the totals gives the expert group offsets.  The four
+// waves place the group's rows (lane l: token l of the group; wave w: slots
+// w, w + 4, ...): a (t, k) row goes to offsets[e] + (rows of e in earlier
+// groups) + (earlier tokens of this group that chose e, from a 64-bit LDS
+// mask).  The expert ids are loaded before the histogram rows, so both loads
+// are in flight together.  Workgroup 0 also writes counts, offsets and the
+// block map (each expert's tiles of at most kTileRows rows, then the shared
+// expert's).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int32_t* __restrict__ hist, int ngp,
                                                                       int T, int K, int E, int has_shared,
@@ -731,6 +734,16 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   constexpr int BM = kTileRows;
 
   mask[e] = 0ull;
+  // this thread's (token, slot) rows: token g*64 + lane, slots wave + 4j
+  constexpr int kSlotsPerWave = (MOE_MAX_TOPK + 3) / 4;
+  const int t = g * kHistTokens + lane;
+  int my[kSlotsPerWave];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerWave; ++j) {
+    const int k = wave + 4 * j;
+    const int id = t < T && k < K ? out.topk_ids[(size_t)t * K + k] : -1;
+    my[j] = (unsigned)id < (unsigned)E ? id : -1;  // ids are produced in range; the check keeps indexing safe
+  }
   // per-expert total and the part owned by groups before g; a row of hist
   // (ngp ints, 16-byte aligned, zero past ng) is read 64 groups per round,
   // all loads of a round in flight together
@@ -803,30 +816,20 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
       }
     }
   }
-  // ---- scatter of this group's rows (first wave, one lane per token) ------
-  const int t = g * kHistTokens + lane;
-  const bool valid = wave == 0 && t < T;
-  int my[MOE_MAX_TOPK];
+  // ---- scatter of this group's rows -------------------------------------------
 #pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-    my[k] = 0;
-    if (valid && k < K) {
-      const int id = out.topk_ids[(size_t)t * K + k];
-      my[k] = (unsigned)id < (unsigned)E ? id : 0;  // ids are produced in range; clamp keeps indexing safe
-      atomicOr(&mask[my[k]], 1ull << lane);
-    }
-  }
+  for (int j = 0; j < kSlotsPerWave; ++j)
+    if (my[j] >= 0) atomicOr(&mask[my[j]], 1ull << lane);
   __syncthreads();
-  if (valid) {
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      if (k < K) {
-        const int x = my[k];
-        const int rank = __popcll(mask[x] & lanes_below());
-        const int p = off_s[x] + before_s[x] + rank;
-        out.sorted_idx[p] = t * K + k;
-        out.inv_pos[(size_t)t * K + k] = p;
-      }
+  for (int j = 0; j < kSlotsPerWave; ++j) {
+    const int x = my[j];
+    if (x >= 0) {
+      const int k = wave + 4 * j;
+      const int rank = __popcll(mask[x] & lanes_below());
+      const int p = off_s[x] + before_s[x] + rank;
+      out.sorted_idx[p] = t * K + k;
+      out.inv_pos[(size_t)t * K + k] = p;
     }
   }
 }
