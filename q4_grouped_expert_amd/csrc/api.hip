@@ -79,7 +79,7 @@ int64_t max_tiles_of(const moe_layer_desc* d) {
 }
 
 struct Layout {
-  size_t hist, ids, w, counts, offsets, sorted, inv, bmap, ntiles, route_end;
+  size_t hist, ids, w, counts, offsets, sorted, inv, bmap, lmap, ntiles, route_end;
   size_t h, y, total;
 };
 
@@ -104,6 +104,7 @@ Layout layout_of(const moe_layer_desc* d, int combine_mode = kDefaultCombine) {
   L.sorted = take(R * 4);
   L.inv = take(R * 4);
   L.bmap = take((size_t)max_tiles_of(d) * 16);
+  L.lmap = take((size_t)max_tiles_of(d) * 16);
   L.ntiles = take(4);
   L.route_end = o;
   L.h = take(rows * (size_t)d->I * 2);
@@ -132,9 +133,12 @@ int check_route_out(const moe_route_out* r) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// launch_map: null, or where routing also writes the tiles in launch order
+// (the layer's own workspace; the GEMMs of the same call read it).
 int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, const float* rb,
-             const moe_route_out* out, void* ws, hipStream_t s) {
+             const moe_route_out* out, void* ws, hipStream_t s, int32_t* launch_map = nullptr) {
   RouteArgs a;
+  a.launch_map = launch_map;
   a.x = x;
   a.w_router = wr;
   a.router_bias = rb;
@@ -166,8 +170,10 @@ int out_mode_of(int mode) {
 // the bound max_tiles_of(d).  zero_out: a gate/up launch also clears T*H
 // floats there (the fused combine's output).
 int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights& w, const moe_route_out* r, void* c,
-            hipStream_t s, int tiles = 0, bool decode = false, float* zero_out = nullptr) {
+            hipStream_t s, int tiles = 0, bool decode = false, float* zero_out = nullptr,
+            const int32_t* launch_map = nullptr) {
   GemmArgs g;
+  g.launch_map = launch_map;
   g.a = reinterpret_cast<const uint16_t*>(a);
   g.codes = w.q ? w.q->codes : nullptr;
   g.scales = w.q ? w.q->scales : nullptr;
@@ -281,6 +287,9 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   }
   void* h = base + L.h;
   void* y = base + L.y;
+  // the prefill routing also lists the tiles in launch order; the decode
+  // routing does not, and its GEMMs walk the block map
+  int32_t* lmap = decode ? nullptr : reinterpret_cast<int32_t*>(base + L.lmap);
   if (decode) {
     DecodeRouteArgs a;
     a.x = x;
@@ -295,7 +304,7 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
     a.has_shared = desc->has_shared;
     a.out = r;
     if ((rc = hip_status(launch_decode_route(a, s)))) return rc;
-  } else if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s))) {
+  } else if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s, lmap))) {
     return rc;
   }
   int tiles = 0;
@@ -316,12 +325,13 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   const bool gemv = decode && desc->T <= kDecodeGemvMaxTokens;
   if (combine_mode == MOE_COMBINE_FUSED) {
     // gate/up clears out, down adds every weighted row into it
-    if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out))) return rc;
-    return do_gemm(desc, MOE_GEMM_DOWN_COMBINE, h, dn, &r, out, s, tiles, gemv);
+    if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out, lmap))) return rc;
+    return do_gemm(desc, MOE_GEMM_DOWN_COMBINE, h, dn, &r, out, s, tiles, gemv, nullptr, lmap);
   }
   const bool bf = combine_mode == MOE_COMBINE_Y_BF16;
-  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv))) return rc;
-  if ((rc = do_gemm(desc, bf ? MOE_GEMM_DOWN_BF16 : MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv))) return rc;
+  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, nullptr, lmap))) return rc;
+  if ((rc = do_gemm(desc, bf ? MOE_GEMM_DOWN_BF16 : MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv, nullptr, lmap)))
+    return rc;
   return do_combine(desc, y, bf ? MOE_DTYPE_BF16 : MOE_DTYPE_F32, &r, out, s);
 }
 

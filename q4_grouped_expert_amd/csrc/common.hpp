@@ -47,6 +47,7 @@ struct RouteArgs {
   const float* router_bias;
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
+  int32_t* launch_map;  // null, or the block map's tiles again, most 16-row subtiles first
 };
 // Routing scratch (expert histograms per 64-token group, router-row norms, a
 // piece-major copy of the router matrix, approximate logits) and launcher.
@@ -65,6 +66,7 @@ struct GemmArgs {
   const uint16_t* s_wbf;    // and the shared expert's [N][Kdim]
   const int32_t* sorted_idx;
   const int32_t* block_map;
+  const int32_t* launch_map;  // null, or the tiles in launch order (most subtiles first)
   const int32_t* n_tiles;
   void* c;                  // output
   int out_mode;             // down: kOutF32, kOutBf16 or kOutCombine
@@ -104,6 +106,7 @@ struct DecodeRouteArgs {
   float* logits;  // workspace [T][E] fp32
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
+  int32_t* launch_map;  // null, or the block map's tiles again, most 16-row subtiles first
 };
 hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, uint16_t* wt, hipStream_t stream);
 hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream);

@@ -45,11 +45,12 @@
 //    16 j, so the SwiGLU epilogue h = bf16(silu(g)*u) happens in registers
 //    and leaves as one 8-byte store per row and subtile; down writes fp32 y
 //    with one 16-byte store per row and subtile.
-//  * Block order: tiles are visited largest first (the block map lists the
-//    shared expert's full tiles last, so it is walked backwards) and the
-//    N-slices of one tile get workgroup ids that are equal modulo 8, which
-//    puts them on the same XCD so the tile's activations are shared in
-//    that XCD's L2.
+//  * Block order: tiles are visited in the routing's launch order, most
+//    16-row subtiles first, so the grid ends on its shortest workgroups
+//    (without that list the block map is walked backwards: the shared
+//    expert's full tiles first), and the N-slices of one tile get workgroup
+//    ids that are equal modulo 8, which puts them on the same XCD so the
+//    tile's activations are shared in that XCD's L2.
 #include <math.h>
 
 #include <type_traits>
@@ -606,13 +607,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   const int grp = b / (kXcds * nN);
   const int rem = b % (kXcds * nN);
   const int nb = rem / kXcds;
-  const int lin = grp * kXcds + rem % kXcds;  // tile rank, largest first
+  const int lin = grp * kXcds + rem % kXcds;  // tile rank in launch order
   if (kGateUp) zero_share(g);
   const int n_tiles = *g.n_tiles;
   if (lin >= n_tiles) return;
-  const int tile = n_tiles - 1 - lin;
-  const int32_t* bmap = g.block_map + 4 * tile;
+  // launch order: the routing's list (most subtiles first), else the block
+  // map backwards (the shared expert's full tiles first)
+  const int32_t* bmap = g.launch_map ? g.launch_map + 4 * lin : g.block_map + 4 * (n_tiles - 1 - lin);
   const int e = bmap[0];
+  {
+    // an entry that routing did not produce (out of range) is skipped, never read through
+    const int r0 = bmap[1], nr = bmap[2];
+    const bool shared_ok = g.s_codes || g.s_wbf;
+    if (e < 0 || e > g.E || (e == g.E && !shared_ok) || nr <= 0 || nr > kTileRows || r0 < 0 ||
+        r0 + nr > g.R + (shared_ok ? g.T : 0))
+      return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;

@@ -720,20 +720,31 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 // mask).  The expert ids are loaded before the histogram rows, so both loads
 // are in flight together.  Workgroup 0 also writes counts, offsets and the
 // block map (each expert's tiles of at most kTileRows rows, then the shared
-// expert's).
+// expert's).  When lmap is set, the last workgroup lists the same tiles again
+// in launch order: most 16-row subtiles first (a GEMM workgroup's time grows
+// with them), so the grouped GEMM starts the longest tiles first and ends on
+// the shortest.  Places come from ballots per subtile count and a scan of the
+// full tiles, so the list is stored in the same phase as the block map.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int32_t* __restrict__ hist, int ngp,
                                                                       int T, int K, int E, int has_shared,
-                                                                      moe_route_out out) {
+                                                                      moe_route_out out, int32_t* __restrict__ lmap) {
   __shared__ int wsum[MOE_MAX_EXPERTS / 64][2];
   __shared__ int before_s[MOE_MAX_EXPERTS], off_s[MOE_MAX_EXPERTS];
   __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
+  constexpr int BM = kTileRows;
+  constexpr int kSub = BM / 16;  // launch order: subtile counts 1..kSub, bucket kSub - count
+  __shared__ int4 pw[kSub];      // launch order: partial tiles of bucket b in wave w (.x .. .w)
+  __shared__ int wfull[MOE_MAX_EXPERTS / 64];  // launch order: full tiles of the experts of wave w
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
   const int g = blockIdx.x;
-  constexpr int BM = kTileRows;
+  // the last workgroup also lists the launch order (every workgroup has the
+  // whole histogram; the first one writes the block map)
+  const bool order = g == (int)gridDim.x - 1 && lmap != nullptr;
 
   mask[e] = 0ull;
+  if (lane < kSub) reinterpret_cast<int*>(&pw[lane])[wave] = 0;  // each wave clears its own column
   // this thread's (token, slot) rows: token g*64 + lane, slots wave + 4j
   constexpr int kSlotsPerWave = (MOE_MAX_TOPK + 3) / 4;
   const int t = g * kHistTokens + lane;
@@ -778,6 +789,34 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
     wsum[wave][0] = ic;
     wsum[wave][1] = it;
   }
+  // launch order, part 1: this expert's full tiles and its last, partial tile
+  // (rem rows, bucket bp); per bucket, the wave's experts with such a tile
+  const int nfull = run / BM, rem = run - nfull * BM;
+  const int bp = kSub - ((rem + 15) >> 4);
+  uint64_t same_b = 0;  // lanes of this wave whose partial tile is in bucket bp
+  if (order) {
+    // the lanes with a partial tile in the same bucket: one ballot per bit of bp
+    same_b = __builtin_amdgcn_ballot_w64(rem > 0);
+#pragma unroll
+    for (int bit = 0; (1 << bit) < kSub; ++bit) {
+      const bool on = (bp >> bit) & 1;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(on);
+      same_b &= on ? m : ~m;
+    }
+    // the first such lane records the bucket's count in this wave (pw starts at zero)
+    if (rem > 0 && (same_b & lanes_below()) == 0) reinterpret_cast<int*>(&pw[bp])[wave] = (int)__popcll(same_b);
+  }
+  int fbw = 0;  // full tiles of the lanes below in this wave (launch order only)
+  if (order) {
+    // one ballot per bit of the full-tile count (at most T / BM)
+    int wtot = 0;
+    for (int bit = 0; (1 << bit) <= T / BM; ++bit) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64((nfull >> bit) & 1);
+      fbw += (int)__popcll(m & lanes_below()) << bit;
+      wtot += (int)__popcll(m) << bit;
+    }
+    if (lane == 0) wfull[wave] = wtot;
+  }
   __syncthreads();
   int bc = 0, bt = 0;
   for (int w = 0; w < wave; ++w) {
@@ -814,6 +853,51 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
         bm[2] = min(BM, T - i * BM);
         bm[3] = 0;
       }
+    }
+  }
+  // ---- launch order, part 2: every tile's place, stored with the block map ----
+  // bucket 0 (16 subtiles): the experts' full tiles in expert order, the
+  // shared expert's full tiles, then the partial tiles of 16 subtiles;
+  // buckets 1.. : partial tiles in expert order, the shared expert's last
+  if (order) {
+    int fb = 0, ftot = 0;  // full tiles of the experts in earlier waves, and of all
+#pragma unroll
+    for (int w = 0; w < MOE_MAX_EXPERTS / 64; ++w) {
+      const int v = wfull[w];
+      fb += w < wave ? v : 0;
+      ftot += v;
+    }
+    const int sfull = has_shared ? T / BM : 0, srem = has_shared ? T - sfull * BM : 0;
+    const int sb = kSub - ((srem + 15) >> 4);  // bucket of the shared expert's partial tile
+    // lane q of each 16-lane row: bucket q (routed partial tiles nq, those of
+    // earlier waves bq); a scan over the row gives the bucket's first place
+    // (bucket 0 opens with every full tile), then each thread reads its own
+    const int q = lane & (kSub - 1);
+    const int4 cq = pw[q];
+    const int nq = cq.x + cq.y + cq.z + cq.w;
+    const int bq = (wave > 0 ? cq.x : 0) + (wave > 1 ? cq.y : 0) + (wave > 2 ? cq.z : 0);
+    const int sz = nq + (srem > 0 && sb == q ? 1 : 0);
+    int inc = sz;
+#pragma unroll
+    for (int o = 1; o < kSub; o <<= 1) {
+      const int v = __shfl_up(inc, o, kSub);
+      if (q >= o) inc += v;
+    }
+    const int startq = ftot + sfull + inc - sz;
+    const int st_p = __shfl(startq, bp & (kSub - 1)), bw = __shfl(bq, bp & (kSub - 1));
+    const int st_s = __shfl(startq, sb & (kSub - 1)), nb_s = __shfl(nq, sb & (kSub - 1));
+    const int f0 = fb + fbw;  // place of this expert's first full tile
+    for (int i = 0; i < nfull; ++i)
+      *reinterpret_cast<int4*>(lmap + 4 * (f0 + i)) = int4{e, off + i * BM, BM, 0};
+    if (rem > 0) {
+      const int pos = st_p + bw + (int)__popcll(same_b & lanes_below());
+      *reinterpret_cast<int4*>(lmap + 4 * pos) = int4{e, off + nfull * BM, rem, 0};
+    }
+    if (e == MOE_MAX_EXPERTS - 1 && has_shared) {
+      const int R = bc + ic;  // total routed rows: the last thread's inclusive scan
+      for (int i = 0; i < sfull; ++i)
+        *reinterpret_cast<int4*>(lmap + 4 * (ftot + i)) = int4{E, R + i * BM, BM, 0};
+      if (srem > 0) *reinterpret_cast<int4*>(lmap + 4 * (st_s + nb_s)) = int4{E, R + sfull * BM, srem, 0};
     }
   }
   // ---- scatter of this group's rows -------------------------------------------
@@ -888,7 +972,7 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_group_kernel, dim3(ng), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ngp, a.T, a.K, a.E,
-                     a.has_shared, a.out);
+                     a.has_shared, a.out, a.launch_map);
   return hipGetLastError();
 }
 

@@ -195,9 +195,10 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     rows = 4096 * 9
     route = B.moe_route_workspace_size(d)
     a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
-    # routing results: ids, w, counts, offsets, sorted_idx, inv_pos, block map, n_tiles
+    # routing results: ids, w, counts, offsets, sorted_idx, inv_pos, block map,
+    # the tiles again in launch order, n_tiles
     results = (a256(4096 * 8 * 4) * 4 + a256(256 * 4) + a256(257 * 4)
-               + a256(B.moe_route_max_tiles(d) * 16) + a256(4))
+               + 2 * a256(B.moe_route_max_tiles(d) * 16) + a256(4))
     h = rows * 512 * 2
     # default: y staged as bf16
     assert big == route + results + h + rows * 2048 * 2
