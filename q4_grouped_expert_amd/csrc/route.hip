@@ -723,8 +723,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 // expert's).  When lmap is set, the last workgroup lists the same tiles again
 // in launch order: most 16-row subtiles first (a GEMM workgroup's time grows
 // with them), so the grouped GEMM starts the longest tiles first and ends on
-// the shortest.  Places come from ballots per subtile count and a scan of the
-// full tiles, so the list is stored in the same phase as the block map.
+// the shortest.  Places come from ballots (the lanes with the same subtile
+// count, the bits of the full-tile counts) and a scan over the 16 counts, so
+// the list is stored in the same phase as the block map.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int32_t* __restrict__ hist, int ngp,
                                                                       int T, int K, int E, int has_shared,
