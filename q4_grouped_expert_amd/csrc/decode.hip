@@ -435,19 +435,23 @@ __global__ __launch_bounds__(512) void decode_route_fused_kernel(const uint16_t*
 // the header comment.
 // ---------------------------------------------------------------------------
 struct GemvLds {
-  // codes of each wave: [segment * 4 + row block][row in block][16-byte chunk]
+  // codes of each wave: [segment * 4 + row block][row in block][16-byte chunk];
+  // once a wave's products are done, the start of its range holds its
+  // partial sums ([2][64] f32x4), so the workgroup needs 37 KB and four fit
+  // on a CU
   uint8_t cl[kGvWaves][kGvSegs * 4][1024];
   uint16_t ssh[32 * kMaxGroupsPerRow];  // [32 rows][gpr] scales
   uint16_t bsh[32 * kMaxGroupsPerRow];  // and biases
-  f32x4 part[kGvWaves][2][64];
 };
+static_assert(2 * 64 * sizeof(f32x4) <= kGvSegs * 4 * 1024, "a wave's partial sums fit its code range");
 
 template <bool kGateUp>
 __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
   auto& cl = sm.cl;
   auto& ssh = sm.ssh;
   auto& bsh = sm.bsh;
-  auto& part = sm.part;
+  // wave w's partial sums, in the code range it alone reads
+  auto part = [&](int w, int j) { return reinterpret_cast<f32x4*>(&cl[w][0][0]) + 64 * j; };
   const int nslice = kGateUp ? g.I / 16 : g.N / 32;
   const int tile = blockIdx.x / nslice, sl = blockIdx.x - tile * nslice;
   if (kGateUp) zero_share(g);
@@ -569,15 +573,17 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
   }
   // lane holds weight rows 4 lg .. 4 lg + 3 of each subtile for tile row ln;
   // the partials of the 4 waves are added in wave order
-  part[wave][0][lane] = acc[0];
-  part[wave][1][lane] = acc[1];
+  // (a wave's LDS operations run in order, so these writes follow its own
+  // last reads of that range)
+  part(wave, 0)[lane] = acc[0];
+  part(wave, 1)[lane] = acc[1];
   __syncthreads();
   if (wave != 0 || ln >= nrows) return;
-  f32x4 s0 = part[0][0][lane], s1 = part[0][1][lane];
+  f32x4 s0 = part(0, 0)[lane], s1 = part(0, 1)[lane];
 #pragma unroll
   for (int w = 1; w < kGvWaves; ++w) {
-    s0 += part[w][0][lane];
-    s1 += part[w][1][lane];
+    s0 += part(w, 0)[lane];
+    s1 += part(w, 1)[lane];
   }
   const int r = row0 + ln;
   if (kGateUp) {
