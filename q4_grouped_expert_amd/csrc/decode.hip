@@ -21,19 +21,20 @@
 //    forms the weights; then the workgroup builds counts, offsets, the stable
 //    permutation and the block map (one tile per expert with rows, then the
 //    shared expert) from the at most 256 (token, slot) pairs.
-//  * Expert GEMVs: a workgroup of 4 waves owns one tile (<= 16 rows of one
-//    expert) and 32 weight rows (gate/up: 16 gate rows and the matching 16
-//    up rows; down: 32 output columns as two subtiles) and splits the
-//    reduction into 4 contiguous ranges of 64-column quant groups, one per
-//    wave.  The work is a few MB spread over the whole chip, so the limit is
+//  * Expert GEMVs: a workgroup owns one tile (<= 16 rows of one expert) and
+//    32 weight rows (gate/up: 16 gate rows and the matching 16 up rows; down:
+//    32 output columns as two subtiles) and splits the reduction into
+//    contiguous ranges of at most 4 quant groups (64 columns each), one per
+//    wave: 8 waves for a 2048-column reduction, 4 up to 1024, with the LDS
+//    sized to match.  The work is a few MB spread over the whole chip, so the limit is
 //    the number of memory requests, not bytes: each wave fetches its codes
 //    as whole 128-byte row segments straight into LDS (8 lanes per segment),
 //    the tile's scales and biases arrive as one 1 KB copy per table half,
 //    and every load of the workgroup is in flight before the first wait.
 //    Each wave dequantizes its codes (fma(q, s, b) in fp32, rounded to bf16)
 //    as the A operand of v_mfma_f32_16x16x32_bf16 with the tile's activation
-//    rows as the B operand.  The 4 partial 16x16 results are added in wave
-//    order through LDS, so the result does not depend on timing.
+//    rows as the B operand.  The waves' partial 16x16 results are added in
+//    wave order through LDS, so the result does not depend on timing.
 //  * Combine: the prefill combine kernel.
 #include <math.h>
 
@@ -47,10 +48,7 @@ namespace moeq4 {
 namespace {
 using namespace gemm;
 
-constexpr int kGvWaves = 4;
-constexpr int kGvThreads = 64 * kGvWaves;
-constexpr int kGvMaxGroups = MOE_MAX_REDUCTION / 64 / kGvWaves;  // quant groups per wave: 8
-constexpr int kGvSegs = kGvMaxGroups * 32 / 128;                 // 128-byte code segments per row and wave: 2
+constexpr int kGvGroupsPerWave = 4;  // quant groups of the reduction per GEMV wave at most
 
 // Maximum of v over the 64 lanes of the wave, returned to every lane: DPP
 // exchanges inside each row of 16 lanes, then the row-pair and half-wave
@@ -434,19 +432,24 @@ __global__ __launch_bounds__(512) void decode_route_fused_kernel(const uint16_t*
 // Split-reduction GEMV of one tile (<= 16 rows) against 32 weight rows, see
 // the header comment.
 // ---------------------------------------------------------------------------
+// NW waves, each taking at most MG = kGvGroupsPerWave quant groups of the
+// reduction: 8 waves and 36 KB for a 2048-column reduction (four workgroups
+// per CU), 4 waves and 18 KB up to 1024 columns (eight per CU)
+template <int NW, int MG>
 struct GemvLds {
+  static constexpr int kSegs = MG * 32 / 128;  // 128-byte code segments per row and wave
   // codes of each wave: [segment * 4 + row block][row in block][16-byte chunk];
   // once a wave's products are done, the start of its range holds its
-  // partial sums ([2][64] f32x4), so the workgroup needs 37 KB and four fit
-  // on a CU
-  uint8_t cl[kGvWaves][kGvSegs * 4][1024];
-  uint16_t ssh[32 * kMaxGroupsPerRow];  // [32 rows][gpr] scales
-  uint16_t bsh[32 * kMaxGroupsPerRow];  // and biases
+  // partial sums ([2][64] f32x4)
+  uint8_t cl[NW][kSegs * 4][1024];
+  uint16_t ssh[32 * NW * MG];  // [32 rows][gpr] scales
+  uint16_t bsh[32 * NW * MG];  // and biases
+  static_assert(2 * 64 * sizeof(f32x4) <= kSegs * 4 * 1024, "a wave's partial sums fit its code range");
 };
-static_assert(2 * 64 * sizeof(f32x4) <= kGvSegs * 4 * 1024, "a wave's partial sums fit its code range");
 
-template <bool kGateUp>
-__device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
+template <bool kGateUp, int NW, int MG>
+__device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds<NW, MG>& sm) {
+  constexpr int kGvSegs = GemvLds<NW, MG>::kSegs;
   auto& cl = sm.cl;
   auto& ssh = sm.ssh;
   auto& bsh = sm.bsh;
@@ -500,24 +503,24 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
   if (kGateUp && arow && row0 + ln < g.R) sidx = g.sorted_idx[row0 + ln];
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the tile's scale and bias tables ([32 rows][gpr] each): wave w
+  // ---- the tile's scale and bias tables ([32 rows][gpr] each): wave w < 4
   // copies half w & 1 (16 rows, 32 gpr bytes <= 1 KB) of table w >> 1; only
   // the lanes inside the half copy (the two halves' LDS ranges are adjacent)
   {
     const int half = wave & 1;
     const uint32_t bytes = 32u * (uint32_t)gpr;
     uint16_t* dst = (wave < 2 ? ssh : bsh) + half * 16 * gpr;
-    if (16u * lane < bytes)
+    if (wave < 4 && 16u * lane < bytes)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? s_rs : b_rs, (__attribute__((address_space(3))) void*)dst,
                                                16, wrow_of(16 * half) * (uint32_t)gpr * 2u + 16u * lane, 0, 0, 0);
   }
-  // ---- this wave's codes: quant groups [g0, g1) (at most kGvMaxGroups), as
+  // ---- this wave's codes: quant groups [g0, g1) (at most MG), as
   // whole 128-byte segments of each of the 32 rows.  DMA (s, rb) fills rows
   // 8 rb .. 8 rb + 7 with segment s: lane l lands at row 8 rb + l/8,
   // physical chunk l%8, and fetches logical chunk (l%8) ^ (l/8), so that the
   // 16 rows one read touches spread over the banks.  Chunks past g1 read
   // zeros.
-  const int g0 = (gpr * wave) / kGvWaves, g1 = (gpr * (wave + 1)) / kGvWaves;
+  const int g0 = (gpr * wave) / NW, g1 = (gpr * (wave + 1)) / NW;
   const int ng = g1 - g0;
   {
     const int r8 = lane >> 3;
@@ -542,9 +545,9 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
     const int src = kGateUp ? (p < g.R ? sidx / g.topk : p - g.R) : p;
     aoff = (uint32_t)src * (uint32_t)Kd * 2u + 32u * lg;
   }
-  u32x4 av[kGvMaxGroups][2];
+  u32x4 av[MG][2];
 #pragma unroll
-  for (int i = 0; i < kGvMaxGroups; ++i)
+  for (int i = 0; i < MG; ++i)
 #pragma unroll
     for (int st = 0; st < 2; ++st)
       av[i][st] = __builtin_bit_cast(
@@ -554,7 +557,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
 
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int i = 0; i < kGvMaxGroups; ++i) {
+  for (int i = 0; i < MG; ++i) {
     if (i < ng) {
       const int sg = i / 4;
       const int c = 2 * (i % 4) + (lg >> 1);  // logical chunk of the segment
@@ -581,7 +584,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
   if (wave != 0 || ln >= nrows) return;
   f32x4 s0 = part(0, 0)[lane], s1 = part(0, 1)[lane];
 #pragma unroll
-  for (int w = 1; w < kGvWaves; ++w) {
+  for (int w = 1; w < NW; ++w) {
     s0 += part(w, 0)[lane];
     s1 += part(w, 1)[lane];
   }
@@ -607,10 +610,10 @@ __device__ __forceinline__ void gemv_body(const GemmArgs& g, GemvLds& sm) {
   }
 }
 
-template <bool kGateUp>
-__global__ __launch_bounds__(kGvThreads) void decode_gemv_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) GemvLds sm;
-  gemv_body<kGateUp>(g, sm);
+template <bool kGateUp, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_gemv_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) GemvLds<NW, kGvGroupsPerWave> sm;
+  gemv_body<kGateUp, NW, kGvGroupsPerWave>(g, sm);
 }
 
 }  // namespace
@@ -639,10 +642,18 @@ hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_gemv(const GemmArgs& g, bool gate_up, hipStream_t stream) {
   const int nslice = gate_up ? g.I / 16 : g.N / 32;
-  if (gate_up)
-    hipLaunchKernelGGL(decode_gemv_kernel<true>, dim3(g.max_tiles * nslice), dim3(kGvThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(decode_gemv_kernel<false>, dim3(g.max_tiles * nslice), dim3(kGvThreads), 0, stream, g);
+  const dim3 grid(g.max_tiles * nslice);
+  // waves: enough for at most kGvGroupsPerWave quant groups each (the
+  // reduction is at most 2048 columns, 32 groups)
+  const bool small = g.Kdim / 64 <= 4 * kGvGroupsPerWave;
+  static_assert(MOE_MAX_REDUCTION / 64 <= 8 * kGvGroupsPerWave, "eight waves cover the longest reduction");
+  if (gate_up) {
+    if (small) hipLaunchKernelGGL((decode_gemv_kernel<true, 4>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((decode_gemv_kernel<true, 8>), grid, dim3(512), 0, stream, g);
+  } else {
+    if (small) hipLaunchKernelGGL((decode_gemv_kernel<false, 4>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((decode_gemv_kernel<false, 8>), grid, dim3(512), 0, stream, g);
+  }
   return hipGetLastError();
 }
 
