@@ -7,10 +7,10 @@
  * exactly what moe_layer_forward computes for the same tokens (the same
  * routing rule and sequential fp32 logits, the same bf16 weights, fp32
  * accumulation) with kernels sized for a handful of rows: an exact router
- * over all experts and a one-workgroup grouping step; for a single token the
- * expert FFN runs as GEMVs that split the reduction over the waves of a
- * workgroup, from two tokens on as the tiled grouped GEMM.  Only the weights
- * of the chosen experts (plus the shared expert) are read.
+ * over all experts and a one-workgroup grouping step; the expert FFN runs
+ * as GEMVs that split the reduction over the waves of a workgroup (every
+ * tile has at most 16 rows).  Only the weights of the chosen experts (plus
+ * the shared expert) are read.
  *
  * Conventions are those of moe_q4.h.
  */

@@ -44,9 +44,6 @@ int device_scratch(void** ptr) {
 namespace {
 
 constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
-// Tokens up to which the decode path runs the expert FFN as split-reduction
-// GEMVs instead of the tiled grouped GEMM.
-constexpr int kDecodeGemvMaxTokens = 4;
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -320,9 +317,9 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   gu.qs = shared_gate_up;
   dn.q = w_down;
   dn.qs = shared_down;
-  // decode: the split-reduction GEMV for a single token, the tiled GEMM from
-  // two tokens on (measured faster there on MI355X)
-  const bool gemv = decode && desc->T <= kDecodeGemvMaxTokens;
+  // decode (at most 16 tokens, so every tile has at most 16 rows): the
+  // split-reduction GEMVs (measured faster than the tiled GEMM at 1-16 tokens)
+  const bool gemv = decode;
   if (combine_mode == MOE_COMBINE_FUSED) {
     // gate/up clears out, down adds every weighted row into it
     if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out, lmap))) return rc;
