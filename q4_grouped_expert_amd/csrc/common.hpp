@@ -106,7 +106,6 @@ struct DecodeRouteArgs {
   float* logits;  // workspace [T][E] fp32
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
-  int32_t* launch_map;  // null, or the block map's tiles again, most 16-row subtiles first
 };
 hipError_t launch_decode_prep(const uint16_t* wr, int H, int E, uint16_t* wt, hipStream_t stream);
 hipError_t launch_decode_route(const DecodeRouteArgs& a, hipStream_t stream);
