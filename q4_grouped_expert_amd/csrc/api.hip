@@ -75,6 +75,20 @@ int64_t max_tiles_of(const moe_layer_desc* d) {
   return n;
 }
 
+// Prompts of at most kSmallPromptTokens tokens run the GEMMs over pieces of
+// at most kSmallRows rows (the small-prompt kernel).
+bool small_prompt(const moe_layer_desc* d) { return d->T <= kSmallPromptTokens; }
+
+// Entries of the launch list: the tiles again, or the small prompt's pieces.
+int64_t max_launch_of(const moe_layer_desc* d) {
+  if (!small_prompt(d)) return max_tiles_of(d);
+  const int64_t R = (int64_t)d->T * d->top_k;
+  const int64_t bm = kSmallRows;
+  int64_t n = R / bm + (R < d->E ? R : d->E);
+  if (d->has_shared) n += (d->T + bm - 1) / bm;
+  return n;
+}
+
 struct Layout {
   size_t hist, ids, w, counts, offsets, sorted, inv, bmap, lmap, ntiles, route_end;
   size_t h, y, total;
@@ -101,8 +115,8 @@ Layout layout_of(const moe_layer_desc* d, int combine_mode = kDefaultCombine) {
   L.sorted = take(R * 4);
   L.inv = take(R * 4);
   L.bmap = take((size_t)max_tiles_of(d) * 16);
-  L.lmap = take((size_t)max_tiles_of(d) * 16);
-  L.ntiles = take(4);
+  L.lmap = take((size_t)max_launch_of(d) * 16);
+  L.ntiles = take(8);  // n_tiles, then the launch list's entry count
   L.route_end = o;
   L.h = take(rows * (size_t)d->I * 2);
   const size_t y_elem = combine_mode == MOE_COMBINE_Y_F32 ? 4 : combine_mode == MOE_COMBINE_Y_BF16 ? 2 : 0;
@@ -132,10 +146,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // launch_map: null, or where routing also writes the tiles in launch order
 // (the layer's own workspace; the GEMMs of the same call read it).
+// n_launch: where its entry count goes; small: the list holds the small
+// prompt's pieces instead of the block map's tiles.
 int do_route(const moe_layer_desc* d, const uint16_t* x, const uint16_t* wr, const float* rb,
-             const moe_route_out* out, void* ws, hipStream_t s, int32_t* launch_map = nullptr) {
+             const moe_route_out* out, void* ws, hipStream_t s, int32_t* launch_map = nullptr,
+             int32_t* n_launch = nullptr, bool small = false) {
   RouteArgs a;
   a.launch_map = launch_map;
+  a.n_launch = n_launch;
+  a.launch_rows = small ? kSmallRows : kTileRows;
   a.x = x;
   a.w_router = wr;
   a.router_bias = rb;
@@ -165,12 +184,15 @@ int out_mode_of(int mode) {
 
 // tiles > 0: launch exactly that many tiles (known on the host) instead of
 // the bound max_tiles_of(d).  zero_out: a gate/up launch also clears T*H
-// floats there (the fused combine's output).
+// floats there (the fused combine's output).  n_launch (with launch_map): the
+// small prompt's piece list and its entry count, for the small-prompt kernel.
 int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights& w, const moe_route_out* r, void* c,
             hipStream_t s, int tiles = 0, bool decode = false, float* zero_out = nullptr,
-            const int32_t* launch_map = nullptr) {
+            const int32_t* launch_map = nullptr, const int32_t* n_launch = nullptr) {
   GemmArgs g;
   g.launch_map = launch_map;
+  g.n_launch = n_launch;
+  g.small = launch_map && n_launch;
   g.a = reinterpret_cast<const uint16_t*>(a);
   g.codes = w.q ? w.q->codes : nullptr;
   g.scales = w.q ? w.q->scales : nullptr;
@@ -193,7 +215,7 @@ int do_gemm(const moe_layer_desc* d, int mode, const void* a, const GemmWeights&
   g.topk = d->top_k;
   g.R = d->T * d->top_k;
   g.I = d->I;
-  g.max_tiles = tiles > 0 ? tiles : (int)max_tiles_of(d);
+  g.max_tiles = tiles > 0 ? tiles : (int)(g.small ? max_launch_of(d) : max_tiles_of(d));
   if (mode == MOE_GEMM_GATE_UP_SWIGLU) {
     g.N = 2 * d->I;
     g.Kdim = d->H;
@@ -284,9 +306,12 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   }
   void* h = base + L.h;
   void* y = base + L.y;
-  // the prefill routing also lists the tiles in launch order; the decode
-  // routing does not, and its GEMMs walk the block map
+  // the prefill routing also lists the tiles in launch order (a small
+  // prompt: its pieces, and their count); the decode routing does not, and
+  // its GEMMs walk the block map
   int32_t* lmap = decode ? nullptr : reinterpret_cast<int32_t*>(base + L.lmap);
+  const bool small = !decode && small_prompt(desc);
+  int32_t* nlaunch = small ? reinterpret_cast<int32_t*>(base + L.ntiles) + 1 : nullptr;
   if (decode) {
     DecodeRouteArgs a;
     a.x = x;
@@ -301,15 +326,18 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
     a.has_shared = desc->has_shared;
     a.out = r;
     if ((rc = hip_status(launch_decode_route(a, s)))) return rc;
-  } else if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s, lmap))) {
+  } else if ((rc = do_route(desc, x, w_router, router_bias, &r, base + L.hist, s, lmap, nlaunch, small))) {
     return rc;
   }
   int tiles = 0;
   if (host_sync) {
     int32_t nt = 0;
-    if (hipMemcpyAsync(&nt, r.n_tiles, sizeof(nt), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+    // the GEMMs' grid: the block map's tiles, or the small prompt's pieces
+    if (hipMemcpyAsync(&nt, small ? nlaunch : r.n_tiles, sizeof(nt), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return MOE_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
-    if (nt <= 0 || nt > max_tiles_of(desc)) return MOE_ERR_HIP;  // routing produced no valid block map
+    // routing produced no valid block map
+    if (nt <= 0 || nt > (small ? max_launch_of(desc) : max_tiles_of(desc))) return MOE_ERR_HIP;
     tiles = nt;
   }
   GemmWeights gu, dn;
@@ -322,12 +350,13 @@ int layer_forward(const moe_layer_desc* desc, const uint16_t* x, const uint16_t*
   const bool gemv = decode;
   if (combine_mode == MOE_COMBINE_FUSED) {
     // gate/up clears out, down adds every weighted row into it
-    if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out, lmap))) return rc;
-    return do_gemm(desc, MOE_GEMM_DOWN_COMBINE, h, dn, &r, out, s, tiles, gemv, nullptr, lmap);
+    if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, out, lmap, nlaunch))) return rc;
+    return do_gemm(desc, MOE_GEMM_DOWN_COMBINE, h, dn, &r, out, s, tiles, gemv, nullptr, lmap, nlaunch);
   }
   const bool bf = combine_mode == MOE_COMBINE_Y_BF16;
-  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, nullptr, lmap))) return rc;
-  if ((rc = do_gemm(desc, bf ? MOE_GEMM_DOWN_BF16 : MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv, nullptr, lmap)))
+  if ((rc = do_gemm(desc, MOE_GEMM_GATE_UP_SWIGLU, x, gu, &r, h, s, tiles, gemv, nullptr, lmap, nlaunch))) return rc;
+  if ((rc = do_gemm(desc, bf ? MOE_GEMM_DOWN_BF16 : MOE_GEMM_DOWN, h, dn, &r, y, s, tiles, gemv, nullptr, lmap,
+                    nlaunch)))
     return rc;
   return do_combine(desc, y, bf ? MOE_DTYPE_BF16 : MOE_DTYPE_F32, &r, out, s);
 }

@@ -18,6 +18,11 @@ constexpr int kWave = 64;
 
 // Rows per GEMM tile in the block map.
 constexpr int kTileRows = 256;
+// Prompts of at most kSmallPromptTokens tokens run the grouped GEMMs over
+// pieces of at most kSmallRows rows (routing lists them), all in the
+// short-tile form of a smaller-LDS kernel, so more workgroups share a CU.
+constexpr int kSmallRows = 64;
+constexpr int kSmallPromptTokens = 1024;
 // Quant groups per weight row the GEMM keeps in LDS (reduction dim <= 2048).
 constexpr int kMaxGroupsPerRow = 32;
 // Tokens per expert-histogram group of the router (the scan runs over groups).
@@ -47,7 +52,14 @@ struct RouteArgs {
   const float* router_bias;
   int T, H, E, K, norm_topk, has_shared;
   moe_route_out out;
-  int32_t* launch_map;  // null, or the block map's tiles again, most 16-row subtiles first
+  // null, or where the grouping also lists the GEMMs' tiles in launch order
+  // (n_launch entries): launch_rows == kTileRows: the block map's tiles, most
+  // 16-row subtiles first; launch_rows == kSmallRows: every expert's rows in
+  // pieces of at most kSmallRows rows, in expert order, the shared expert's
+  // last
+  int32_t* launch_map;
+  int32_t* n_launch;
+  int launch_rows;
 };
 // Routing scratch (expert histograms per 64-token group, router-row norms, a
 // piece-major copy of the router matrix, approximate logits) and launcher.
@@ -66,7 +78,9 @@ struct GemmArgs {
   const uint16_t* s_wbf;    // and the shared expert's [N][Kdim]
   const int32_t* sorted_idx;
   const int32_t* block_map;
-  const int32_t* launch_map;  // null, or the tiles in launch order (most subtiles first)
+  const int32_t* launch_map;  // null, or the tiles in launch order
+  const int32_t* n_launch;    // with small: the list's entry count (else n_tiles bounds it)
+  int small;                  // the list holds pieces of at most kSmallRows rows: the small kernel
   const int32_t* n_tiles;
   void* c;                  // output
   int out_mode;             // down: kOutF32, kOutBf16 or kOutCombine

@@ -256,7 +256,7 @@ __device__ __forceinline__ u32x2 swiglu4(const f32x4& gt, const f32x4& up) {
 // LDS layout: row r of the slice in array r / RPA, its 16-byte chunk c at
 // chunk c ^ (r % CH), so the 16 rows one write instruction touches fall on
 // different banks.
-template <bool kGateUp, int MSUB>
+template <bool kGateUp, int MSUB, int QE = kQElems>  // QE: bf16 elements per LDS array
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, const LdsQ& L,
                                            const f32x4 (&acc)[MSUB][NS]) {
   if (!kGateUp && g.out_mode != kOutBf16) {
@@ -268,8 +268,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const TileCtx& t, 
   const int ln = lane & 15, lg = lane >> 4;
   constexpr int OC = kGateUp ? BN / 2 : BN;  // bf16 output columns of the slice
   constexpr int CH = OC / 8;                 // 16-byte chunks per row
-  constexpr int RPA = kQElems / OC;          // slice rows per LDS array
-  static_assert(MSUB * 16 <= 4 * RPA, "the staged tile fits the four arrays");
+  constexpr int RPA = QE / OC;               // slice rows per LDS array
+  static_assert(MSUB * 16 <= 3 * RPA || (QE == kQElems && MSUB * 16 <= 4 * RPA), "the staged tile fits the arrays");
   auto at = [&](int r, int c) { return lds_q(L, r / RPA) + (r % RPA) * OC + ((c ^ (r % CH)) * 8); };
   wait_vmcnt<0>();
   __syncthreads();  // every wave's ring DMAs landed and every wave is past its last LDS read
@@ -456,7 +456,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, c
   if (kt < nk) stage(kNext, kSlot1, kt, bq[1], bq[0]);
   wait_vmcnt<0>();  // no direct-to-LDS write outlives the tile
 
-  store_tile<kGateUp, MSUB>(g, t, L, acc);
+  store_tile<kGateUp, MSUB, kQElems>(g, t, L, acc);
 }
 
 // Short tiles (<= 4 row subtiles) have little matrix work per stage, so the
@@ -469,12 +469,18 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const TileCtx& t, c
 // start at zero and every stage accumulates: the same MFMA sequence as the
 // 2-stage form, so both give bit-identical results.
 constexpr int kRingMaxSub = 4;  // row subtiles up to which a tile takes the ring form
-constexpr int kRing = 4;
 constexpr int kRingW = 4096;  // bf16-element offset of a slot's codes
+// The small-prompt kernel's LDS arrays: one ring slot each (activations of 64
+// rows, then the codes), 12 KB instead of 16 KB, and three of them.
+constexpr int kSmallQElems = kRingW + NWAVES * 512;
 
-template <bool kGateUp, int MSUB>
+// kRing: slots (4: loads three stages ahead; the small-prompt kernel's 3: two
+// stages ahead, in less LDS)
+template <bool kGateUp, int MSUB, int kRing, int QE>
 __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx& t, const LdsQ& L,
                                                uint16_t* __restrict__ Ssh, uint16_t* __restrict__ Bsh) {
+  static_assert(kRing == 3 || kRing == 4, "ring slots");
+  static_assert(kRingW + NWAVES * 512 <= QE, "a slot fits its array");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
   const int ln = lane & 15, lg = lane >> 4;
@@ -483,7 +489,7 @@ __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx&
   constexpr int ADMA = (MSUB * 16 + ROWS_PER_DMA - 1) / ROWS_PER_DMA;
   constexpr int kPerStage = ADMA + 1;  // vector-memory loads per wave per stage
   static_assert(ADMA * ROWS_PER_DMA * BK <= kRingW, "activations overlap the codes");
-  static_assert(kRingW + NWAVES * 512 <= kQElems, "slot overflow");
+  static_assert(kRingW + NWAVES * 512 <= kSmallQElems, "slot overflow");
 
   uint32_t adoff[ADMA];
   activation_offsets<kGateUp, MSUB>(g, t, adoff);
@@ -538,9 +544,9 @@ __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx&
   wait_vmcnt<(kRing - 2) * kPerStage>();  // the tables and stage 0 landed
   __builtin_amdgcn_s_barrier();
 
-  // Stage kt in slot S: load stage kt + 3 into slot S - 1 (read in stage
-  // kt - 1, free since the last barrier), dequantize this stage's codes,
-  // run the MFMA regions, wait until stage kt + 1 has landed, barrier.
+  // Stage kt in slot S: load stage kt + kRing - 1 into slot S - 1 (read in
+  // stage kt - 1, free since the last barrier), dequantize this stage's
+  // codes, run the MFMA regions, wait until stage kt + 1 has landed, barrier.
   auto stage = [&](auto slot, int kt) {
     constexpr int S = decltype(slot)::value;
     constexpr int LS = (S + kRing - 1) % kRing;
@@ -575,28 +581,43 @@ __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx&
   const std::integral_constant<int, 2> kS2;
   const std::integral_constant<int, 3> kS3;
   int kt = 0;
-  for (; kt + kRing <= nk; kt += kRing) {
-    stage(kS0, kt);
-    stage(kS1, kt + 1);
-    stage(kS2, kt + 2);
-    stage(kS3, kt + 3);
+  if constexpr (kRing == 4) {
+    for (; kt + kRing <= nk; kt += kRing) {
+      stage(kS0, kt);
+      stage(kS1, kt + 1);
+      stage(kS2, kt + 2);
+      stage(kS3, kt + 3);
+    }
+    if (kt < nk) stage(kS0, kt);
+    if (kt + 1 < nk) stage(kS1, kt + 1);
+    if (kt + 2 < nk) stage(kS2, kt + 2);
+  } else {
+    for (; kt + kRing <= nk; kt += kRing) {
+      stage(kS0, kt);
+      stage(kS1, kt + 1);
+      stage(kS2, kt + 2);
+    }
+    if (kt < nk) stage(kS0, kt);
+    if (kt + 1 < nk) stage(kS1, kt + 1);
   }
-  if (kt < nk) stage(kS0, kt);
-  if (kt + 1 < nk) stage(kS1, kt + 1);
-  if (kt + 2 < nk) stage(kS2, kt + 2);
   wait_vmcnt<0>();  // no direct-to-LDS write outlives the tile
-  store_tile<kGateUp, MSUB>(g, t, L, acc);
+  store_tile<kGateUp, MSUB, QE>(g, t, L, acc);
 }
 
-template <bool kGateUp, bool kBf16W>
-__global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
+// kSmall: the small-prompt kernel, over a list of pieces of at most
+// kSmallRows rows, all in the short-tile form with a 3-slot ring: 52 KB of
+// LDS (gate/up) and three workgroups per CU instead of two.
+template <bool kGateUp, bool kBf16W, bool kSmall>
+__global__ __launch_bounds__(NT, kSmall ? 3 : 2) void gemm_q4_kernel(GemmArgs g) {
   // activation ring: two stages of [256 rows][64] bf16, as four arrays of
-  // 128 rows (short tiles: a 4-slot ring of activations and codes)
-  __shared__ __attribute__((aligned(16))) uint16_t Lq0[kQElems];
-  __shared__ __attribute__((aligned(16))) uint16_t Lq1[kQElems];
-  __shared__ __attribute__((aligned(16))) uint16_t Lq2[kQElems];
-  __shared__ __attribute__((aligned(16))) uint16_t Lq3[kQElems];
-  const LdsQ L{Lq0, Lq1, Lq2, Lq3};
+  // 128 rows (short tiles: a 4-slot ring of activations and codes); the
+  // small kernel: three arrays of one 3-slot ring's slot each
+  constexpr int QE = kSmall ? kSmallQElems : kQElems;
+  __shared__ __attribute__((aligned(16))) uint16_t Lq0[QE];
+  __shared__ __attribute__((aligned(16))) uint16_t Lq1[QE];
+  __shared__ __attribute__((aligned(16))) uint16_t Lq2[QE];
+  __shared__ __attribute__((aligned(16))) uint16_t Lq3[kSmall ? 8 : kQElems];  // not used by the small kernel
+  const LdsQ L{Lq0, Lq1, Lq2, kSmall ? Lq2 : Lq3};
   // the tile's scales and biases: [128 weight rows][<= 32 groups] bf16 each
   __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kMaxGroups];
   __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kMaxGroups];
@@ -609,18 +630,19 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   const int nb = rem / kXcds;
   const int lin = grp * kXcds + rem % kXcds;  // tile rank in launch order
   if (kGateUp) zero_share(g);
-  const int n_tiles = *g.n_tiles;
+  const int n_tiles = kSmall ? *g.n_launch : *g.n_tiles;
   if (lin >= n_tiles) return;
-  // launch order: the routing's list (most subtiles first), else the block
-  // map backwards (the shared expert's full tiles first)
+  // launch order: the routing's list (most subtiles first, or the small
+  // kernel's pieces), else the block map backwards (the shared expert's full
+  // tiles first)
   const int32_t* bmap = g.launch_map ? g.launch_map + 4 * lin : g.block_map + 4 * (n_tiles - 1 - lin);
   const int e = bmap[0];
   {
     // an entry that routing did not produce (out of range) is skipped, never read through
     const int r0 = bmap[1], nr = bmap[2];
     const bool shared_ok = g.s_codes || g.s_wbf;
-    if (e < 0 || e > g.E || (e == g.E && !shared_ok) || nr <= 0 || nr > kTileRows || r0 < 0 ||
-        r0 + nr > g.R + (shared_ok ? g.T : 0))
+    if (e < 0 || e > g.E || (e == g.E && !shared_ok) || nr <= 0 || nr > (kSmall ? kSmallRows : kTileRows) ||
+        r0 < 0 || r0 + nr > g.R + (shared_ok ? g.T : 0))
       return;
   }
 
@@ -716,35 +738,47 @@ __global__ __launch_bounds__(NT, 2) void gemm_q4_kernel(GemmArgs g) {
   }
 
   const int msub = (t.nrows + 15) >> 4;
-  switch (msub) {
-    case 1:
-      if constexpr (!kBf16W) tile_body_ring<kGateUp, 1>(g, t, L, Ssh, Bsh);
-      else tile_body<kGateUp, kBf16W, 1>(g, t, L, Ssh, Bsh);
-      break;
-    case 2:
-      if constexpr (!kBf16W && kRingMaxSub >= 2) tile_body_ring<kGateUp, 2>(g, t, L, Ssh, Bsh);
-      else tile_body<kGateUp, kBf16W, 2>(g, t, L, Ssh, Bsh);
-      break;
-    case 3:
-      if constexpr (!kBf16W && kRingMaxSub >= 3) tile_body_ring<kGateUp, 3>(g, t, L, Ssh, Bsh);
-      else tile_body<kGateUp, kBf16W, 3>(g, t, L, Ssh, Bsh);
-      break;
-    case 4:
-      if constexpr (!kBf16W && kRingMaxSub >= 4) tile_body_ring<kGateUp, 4>(g, t, L, Ssh, Bsh);
-      else tile_body<kGateUp, kBf16W, 4>(g, t, L, Ssh, Bsh);
-      break;
-    case 5: tile_body<kGateUp, kBf16W, 5>(g, t, L, Ssh, Bsh); break;
-    case 6: tile_body<kGateUp, kBf16W, 6>(g, t, L, Ssh, Bsh); break;
-    case 7: tile_body<kGateUp, kBf16W, 7>(g, t, L, Ssh, Bsh); break;
-    case 8: tile_body<kGateUp, kBf16W, 8>(g, t, L, Ssh, Bsh); break;
-    case 9: tile_body<kGateUp, kBf16W, 9>(g, t, L, Ssh, Bsh); break;
-    case 10: tile_body<kGateUp, kBf16W, 10>(g, t, L, Ssh, Bsh); break;
-    case 11: tile_body<kGateUp, kBf16W, 11>(g, t, L, Ssh, Bsh); break;
-    case 12: tile_body<kGateUp, kBf16W, 12>(g, t, L, Ssh, Bsh); break;
-    case 13: tile_body<kGateUp, kBf16W, 13>(g, t, L, Ssh, Bsh); break;
-    case 14: tile_body<kGateUp, kBf16W, 14>(g, t, L, Ssh, Bsh); break;
-    case 15: tile_body<kGateUp, kBf16W, 15>(g, t, L, Ssh, Bsh); break;
-    default: tile_body<kGateUp, kBf16W, 16>(g, t, L, Ssh, Bsh); break;
+  if constexpr (kSmall) {
+    static_assert(!kBf16W && kSmallRows == 16 * kRingMaxSub, "the small kernel runs 4-bit pieces of the ring form");
+    switch (msub) {
+      case 1: tile_body_ring<kGateUp, 1, 3, QE>(g, t, L, Ssh, Bsh); break;
+      case 2: tile_body_ring<kGateUp, 2, 3, QE>(g, t, L, Ssh, Bsh); break;
+      case 3: tile_body_ring<kGateUp, 3, 3, QE>(g, t, L, Ssh, Bsh); break;
+      default: tile_body_ring<kGateUp, 4, 3, QE>(g, t, L, Ssh, Bsh); break;
+    }
+  } else {
+    // (not instantiated in the small kernel, so no tile-body instance is
+    // shared by two kernel instances)
+    switch (msub) {
+      case 1:
+        if constexpr (!kBf16W) tile_body_ring<kGateUp, 1, 4, QE>(g, t, L, Ssh, Bsh);
+        else tile_body<kGateUp, kBf16W, 1>(g, t, L, Ssh, Bsh);
+        break;
+      case 2:
+        if constexpr (!kBf16W && kRingMaxSub >= 2) tile_body_ring<kGateUp, 2, 4, QE>(g, t, L, Ssh, Bsh);
+        else tile_body<kGateUp, kBf16W, 2>(g, t, L, Ssh, Bsh);
+        break;
+      case 3:
+        if constexpr (!kBf16W && kRingMaxSub >= 3) tile_body_ring<kGateUp, 3, 4, QE>(g, t, L, Ssh, Bsh);
+        else tile_body<kGateUp, kBf16W, 3>(g, t, L, Ssh, Bsh);
+        break;
+      case 4:
+        if constexpr (!kBf16W && kRingMaxSub >= 4) tile_body_ring<kGateUp, 4, 4, QE>(g, t, L, Ssh, Bsh);
+        else tile_body<kGateUp, kBf16W, 4>(g, t, L, Ssh, Bsh);
+        break;
+      case 5: tile_body<kGateUp, kBf16W, 5>(g, t, L, Ssh, Bsh); break;
+      case 6: tile_body<kGateUp, kBf16W, 6>(g, t, L, Ssh, Bsh); break;
+      case 7: tile_body<kGateUp, kBf16W, 7>(g, t, L, Ssh, Bsh); break;
+      case 8: tile_body<kGateUp, kBf16W, 8>(g, t, L, Ssh, Bsh); break;
+      case 9: tile_body<kGateUp, kBf16W, 9>(g, t, L, Ssh, Bsh); break;
+      case 10: tile_body<kGateUp, kBf16W, 10>(g, t, L, Ssh, Bsh); break;
+      case 11: tile_body<kGateUp, kBf16W, 11>(g, t, L, Ssh, Bsh); break;
+      case 12: tile_body<kGateUp, kBf16W, 12>(g, t, L, Ssh, Bsh); break;
+      case 13: tile_body<kGateUp, kBf16W, 13>(g, t, L, Ssh, Bsh); break;
+      case 14: tile_body<kGateUp, kBf16W, 14>(g, t, L, Ssh, Bsh); break;
+      case 15: tile_body<kGateUp, kBf16W, 15>(g, t, L, Ssh, Bsh); break;
+      default: tile_body<kGateUp, kBf16W, 16>(g, t, L, Ssh, Bsh); break;
+    }
   }
 }
 
@@ -754,19 +788,19 @@ int grid_blocks(int max_tiles, int nN) { return (max_tiles + kXcds - 1) / kXcds 
 
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.N + BN - 1) / BN;
-  if (g.wbf)
-    hipLaunchKernelGGL((gemm_q4_kernel<false, true>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_q4_kernel<false, false>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  const dim3 grid(grid_blocks(g.max_tiles, nN));
+  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<false, true, false>), grid, dim3(NT), 0, stream, g);
+  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<false, false, true>), grid, dim3(NT), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_q4_kernel<false, false, false>), grid, dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.I + BN / 2 - 1) / (BN / 2);
-  if (g.wbf)
-    hipLaunchKernelGGL((gemm_q4_kernel<true, true>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_q4_kernel<true, false>), dim3(grid_blocks(g.max_tiles, nN)), dim3(NT), 0, stream, g);
+  const dim3 grid(grid_blocks(g.max_tiles, nN));
+  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<true, true, false>), grid, dim3(NT), 0, stream, g);
+  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<true, false, true>), grid, dim3(NT), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_q4_kernel<true, false, false>), grid, dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 

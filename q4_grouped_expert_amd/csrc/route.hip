@@ -723,13 +723,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 // expert's).  When lmap is set, the last workgroup lists the same tiles again
 // in launch order: most 16-row subtiles first (a GEMM workgroup's time grows
 // with them), so the grouped GEMM starts the longest tiles first and ends on
-// the shortest.  Places come from ballots (the lanes with the same subtile
-// count, the bits of the full-tile counts) and a scan over the 16 counts, so
-// the list is stored in the same phase as the block map.
+// the shortest; or, with launch_rows below kTileRows, every expert's rows cut
+// into pieces of at most launch_rows rows in expert order (the shared
+// expert's last) for the small-prompt GEMMs; n_launch entries in all.
+// Places come from ballots (the lanes with the same subtile count, the bits
+// of the full-tile counts) and a scan over the 16 counts, so the list is
+// stored in the same phase as the block map.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int32_t* __restrict__ hist, int ngp,
                                                                       int T, int K, int E, int has_shared,
-                                                                      moe_route_out out, int32_t* __restrict__ lmap) {
+                                                                      moe_route_out out, int32_t* __restrict__ lmap,
+                                                                      int32_t* __restrict__ n_launch, int launch_rows) {
   __shared__ int wsum[MOE_MAX_EXPERTS / 64][2];
   __shared__ int before_s[MOE_MAX_EXPERTS], off_s[MOE_MAX_EXPERTS];
   __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
@@ -743,6 +747,10 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   // the last workgroup also lists the launch order (every workgroup has the
   // whole histogram; the first one writes the block map)
   const bool order = g == (int)gridDim.x - 1 && lmap != nullptr;
+  // a piece list (launch_rows < BM): pieces of LR rows in expert order, every
+  // piece counted as a full tile (no partial-tile buckets)
+  const bool pieces = launch_rows < BM;
+  const int LR = pieces ? launch_rows : BM;
 
   mask[e] = 0ull;
   if (lane < kSub) reinterpret_cast<int*>(&pw[lane])[wave] = 0;  // each wave clears its own column
@@ -792,10 +800,10 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   }
   // launch order, part 1: this expert's full tiles and its last, partial tile
   // (rem rows, bucket bp); per bucket, the wave's experts with such a tile
-  const int nfull = run / BM, rem = run - nfull * BM;
+  const int nfull = pieces ? (run + LR - 1) / LR : run / BM, rem = pieces ? 0 : run - nfull * BM;
   const int bp = kSub - ((rem + 15) >> 4);
   uint64_t same_b = 0;  // lanes of this wave whose partial tile is in bucket bp
-  if (order) {
+  if (order && !pieces) {
     // the lanes with a partial tile in the same bucket: one ballot per bit of bp
     same_b = __builtin_amdgcn_ballot_w64(rem > 0);
 #pragma unroll
@@ -809,9 +817,9 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   }
   int fbw = 0;  // full tiles of the lanes below in this wave (launch order only)
   if (order) {
-    // one ballot per bit of the full-tile count (at most T / BM)
+    // one ballot per bit of the full-tile count (at most ceil(T / LR))
     int wtot = 0;
-    for (int bit = 0; (1 << bit) <= T / BM; ++bit) {
+    for (int bit = 0; (1 << bit) <= (T + LR - 1) / LR; ++bit) {
       const uint64_t m = __builtin_amdgcn_ballot_w64((nfull >> bit) & 1);
       fbw += (int)__popcll(m & lanes_below()) << bit;
       wtot += (int)__popcll(m) << bit;
@@ -868,7 +876,8 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
       fb += w < wave ? v : 0;
       ftot += v;
     }
-    const int sfull = has_shared ? T / BM : 0, srem = has_shared ? T - sfull * BM : 0;
+    const int sfull = has_shared ? (pieces ? (T + LR - 1) / LR : T / BM) : 0;
+    const int srem = has_shared && !pieces ? T - sfull * BM : 0;
     const int sb = kSub - ((srem + 15) >> 4);  // bucket of the shared expert's partial tile
     // lane q of each 16-lane row: bucket q (routed partial tiles nq, those of
     // earlier waves bq); a scan over the row gives the bucket's first place
@@ -887,9 +896,11 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
     const int startq = ftot + sfull + inc - sz;
     const int st_p = __shfl(startq, bp & (kSub - 1)), bw = __shfl(bq, bp & (kSub - 1));
     const int st_s = __shfl(startq, sb & (kSub - 1)), nb_s = __shfl(nq, sb & (kSub - 1));
+    const int ntot = ftot + sfull + __shfl(inc, kSub - 1);  // every tile or piece (lane 15 holds the buckets' total)
+    if (e == 0 && n_launch) *n_launch = ntot;
     const int f0 = fb + fbw;  // place of this expert's first full tile
     for (int i = 0; i < nfull; ++i)
-      *reinterpret_cast<int4*>(lmap + 4 * (f0 + i)) = int4{e, off + i * BM, BM, 0};
+      *reinterpret_cast<int4*>(lmap + 4 * (f0 + i)) = int4{e, off + i * LR, min(LR, run - i * LR), 0};
     if (rem > 0) {
       const int pos = st_p + bw + (int)__popcll(same_b & lanes_below());
       *reinterpret_cast<int4*>(lmap + 4 * pos) = int4{e, off + nfull * BM, rem, 0};
@@ -897,7 +908,7 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
     if (e == MOE_MAX_EXPERTS - 1 && has_shared) {
       const int R = bc + ic;  // total routed rows: the last thread's inclusive scan
       for (int i = 0; i < sfull; ++i)
-        *reinterpret_cast<int4*>(lmap + 4 * (ftot + i)) = int4{E, R + i * BM, BM, 0};
+        *reinterpret_cast<int4*>(lmap + 4 * (ftot + i)) = int4{E, R + i * LR, min(LR, T - i * LR), 0};
       if (srem > 0) *reinterpret_cast<int4*>(lmap + 4 * (st_s + nb_s)) = int4{E, R + sfull * BM, srem, 0};
     }
   }
@@ -973,7 +984,7 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t stream) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_group_kernel, dim3(ng), dim3(MOE_MAX_EXPERTS), 0, stream, hist, ngp, a.T, a.K, a.E,
-                     a.has_shared, a.out, a.launch_map);
+                     a.has_shared, a.out, a.launch_map, a.n_launch, a.launch_rows);
   return hipGetLastError();
 }
 

@@ -207,6 +207,13 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     # the fused combine stages no y at all
     assert B.moe_layer_workspace_size_ex(d, B.MOE_COMBINE_FUSED) == route + results + h
     assert big > small
+    # a prompt of at most 1024 tokens lists its rows in pieces of at most 64
+    # rows (one more list entry per 64 routed rows) instead of the tiles again
+    ds = B.layer_desc(512, 2048, 512, 256, 8)
+    pieces = 512 * 8 // 64 + 256 + 512 // 64  # the shared expert: 8 more
+    results_s = (a256(512 * 8 * 4) * 4 + a256(256 * 4) + a256(257 * 4)
+                 + a256(B.moe_route_max_tiles(ds) * 16) + a256(pieces * 16) + a256(4))
+    assert small == B.moe_route_workspace_size(ds) + results_s + 512 * 9 * 512 * 2 + 512 * 9 * 2048 * 2
     # routing scratch: expert histograms [E][64-token groups rounded up to 4]
     # int32, 256 router-row norms, the piece-major router copy [H/8][E][8]
     # bf16 and approximate logits [T][E] fp32 (4096 tokens: one split)

@@ -62,6 +62,11 @@ SMALL = {
     "H2048_I2048": gen.custom_shape(40, 2048, 2048, 8, 2, seed=34),
     # an expert count that is not a multiple of 4 (router lanes past E)
     "E10_K3": gen.custom_shape(45, 256, 128, 10, 3, seed=35),
+    # the largest prompt whose GEMMs run over pieces of at most 64 rows, and
+    # one token more (tiles of up to 256 rows); a skewed router gives experts
+    # of several pieces
+    "pieces_T1024": gen.custom_shape(1024, 128, 64, 12, 3, zipf_s=1.1, seed=37),
+    "tiles_T1025": gen.custom_shape(1025, 128, 64, 12, 3, zipf_s=1.1, seed=38),
 }
 
 
