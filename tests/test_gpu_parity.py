@@ -67,6 +67,11 @@ SMALL = {
     # of several pieces
     "pieces_T1024": gen.custom_shape(1024, 128, 64, 12, 3, zipf_s=1.1, seed=37),
     "tiles_T1025": gen.custom_shape(1025, 128, 64, 12, 3, zipf_s=1.1, seed=38),
+    # small prompts whose down GEMM's last 128-column slice is half outside
+    # the matrix (H = 384), and with an odd count of quant groups per row in
+    # the down GEMM (I = 192)
+    "pieces_H384": gen.custom_shape(200, 384, 128, 16, 4, seed=39),
+    "odd_groups_I192": gen.custom_shape(200, 256, 192, 16, 4, seed=40),
 }
 
 
