@@ -172,7 +172,7 @@ int moe_route_max_tiles(const moe_layer_desc* desc, int32_t* max_tiles);
 /* Workspace bytes of moe_layer_forward for `desc` (host-only, pure): the
  * routing scratch, the routing results (used when route_or_null is NULL),
  * the GEMMs' launch list (the block map's tiles again, in the order the
- * GEMMs start them: max_tiles entries of 16 bytes; for T <= 1024 instead
+ * GEMMs start them: max_tiles entries of 16 bytes; for T <= 1536 instead
  * every expert's rows in pieces of at most 64 rows: up to R/64 + min(R, E)
  * (+ ceil(T/64)) entries, and their count), h bf16 [R(+T)][I] and
  * y bf16 [R(+T)][H], each piece 256-byte aligned.  The

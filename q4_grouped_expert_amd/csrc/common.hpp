@@ -22,7 +22,7 @@ constexpr int kTileRows = 256;
 // pieces of at most kSmallRows rows (routing lists them), all in the
 // short-tile form of a smaller-LDS kernel, so more workgroups share a CU.
 constexpr int kSmallRows = 64;
-constexpr int kSmallPromptTokens = 1024;
+constexpr int kSmallPromptTokens = 1536;
 // Quant groups per weight row the GEMM keeps in LDS (reduction dim <= 2048).
 constexpr int kMaxGroupsPerRow = 32;
 // Tokens per expert-histogram group of the router (the scan runs over groups).

@@ -207,7 +207,7 @@ def test_workspace_size_grows_with_tokens_and_covers_h_and_y():
     # the fused combine stages no y at all
     assert B.moe_layer_workspace_size_ex(d, B.MOE_COMBINE_FUSED) == route + results + h
     assert big > small
-    # a prompt of at most 1024 tokens lists its rows in pieces of at most 64
+    # a prompt of at most 1536 tokens lists its rows in pieces of at most 64
     # rows (one more list entry per 64 routed rows) instead of the tiles again
     ds = B.layer_desc(512, 2048, 512, 256, 8)
     pieces = 512 * 8 // 64 + 256 + 512 // 64  # the shared expert: 8 more

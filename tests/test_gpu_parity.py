@@ -65,8 +65,8 @@ SMALL = {
     # the largest prompt whose GEMMs run over pieces of at most 64 rows, and
     # one token more (tiles of up to 256 rows); a skewed router gives experts
     # of several pieces
-    "pieces_T1024": gen.custom_shape(1024, 128, 64, 12, 3, zipf_s=1.1, seed=37),
-    "tiles_T1025": gen.custom_shape(1025, 128, 64, 12, 3, zipf_s=1.1, seed=38),
+    "pieces_T1536": gen.custom_shape(1536, 128, 64, 12, 3, zipf_s=1.1, seed=37),
+    "tiles_T1537": gen.custom_shape(1537, 128, 64, 12, 3, zipf_s=1.1, seed=38),
     # small prompts whose down GEMM's last 128-column slice is half outside
     # the matrix (H = 384), and with an odd count of quant groups per row in
     # the down GEMM (I = 192)
