@@ -724,8 +724,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a, const fl
 // in launch order: most 16-row subtiles first (a GEMM workgroup's time grows
 // with them), so the grouped GEMM starts the longest tiles first and ends on
 // the shortest; or, with launch_rows below kTileRows, every expert's rows cut
-// into pieces of at most launch_rows rows in expert order (the shared
-// expert's last) for the small-prompt GEMMs; n_launch entries in all.
+// into pieces of at most launch_rows rows for the small-prompt GEMMs, in the
+// same order (full pieces first, then the partial ones by subtile count);
+// n_launch entries in all.
 // Places come from ballots (the lanes with the same subtile count, the bits
 // of the full-tile counts) and a scan over the 16 counts, so the list is
 // stored in the same phase as the block map.
@@ -747,8 +748,8 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   // the last workgroup also lists the launch order (every workgroup has the
   // whole histogram; the first one writes the block map)
   const bool order = g == (int)gridDim.x - 1 && lmap != nullptr;
-  // a piece list (launch_rows < BM): pieces of LR rows in expert order, every
-  // piece counted as a full tile (no partial-tile buckets)
+  // a piece list (launch_rows < BM): pieces of at most LR rows, in the same
+  // order as tiles (full pieces first, then the partial ones by subtile count)
   const bool pieces = launch_rows < BM;
   const int LR = pieces ? launch_rows : BM;
 
@@ -800,10 +801,10 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
   }
   // launch order, part 1: this expert's full tiles and its last, partial tile
   // (rem rows, bucket bp); per bucket, the wave's experts with such a tile
-  const int nfull = pieces ? (run + LR - 1) / LR : run / BM, rem = pieces ? 0 : run - nfull * BM;
+  const int nfull = run / LR, rem = run - nfull * LR;
   const int bp = kSub - ((rem + 15) >> 4);
   uint64_t same_b = 0;  // lanes of this wave whose partial tile is in bucket bp
-  if (order && !pieces) {
+  if (order) {
     // the lanes with a partial tile in the same bucket: one ballot per bit of bp
     same_b = __builtin_amdgcn_ballot_w64(rem > 0);
 #pragma unroll
@@ -876,8 +877,8 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
       fb += w < wave ? v : 0;
       ftot += v;
     }
-    const int sfull = has_shared ? (pieces ? (T + LR - 1) / LR : T / BM) : 0;
-    const int srem = has_shared && !pieces ? T - sfull * BM : 0;
+    const int sfull = has_shared ? T / LR : 0;
+    const int srem = has_shared ? T - sfull * LR : 0;
     const int sb = kSub - ((srem + 15) >> 4);  // bucket of the shared expert's partial tile
     // lane q of each 16-lane row: bucket q (routed partial tiles nq, those of
     // earlier waves bq); a scan over the row gives the bucket's first place
@@ -900,16 +901,16 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
     if (e == 0 && n_launch) *n_launch = ntot;
     const int f0 = fb + fbw;  // place of this expert's first full tile
     for (int i = 0; i < nfull; ++i)
-      *reinterpret_cast<int4*>(lmap + 4 * (f0 + i)) = int4{e, off + i * LR, min(LR, run - i * LR), 0};
+      *reinterpret_cast<int4*>(lmap + 4 * (f0 + i)) = int4{e, off + i * LR, LR, 0};
     if (rem > 0) {
       const int pos = st_p + bw + (int)__popcll(same_b & lanes_below());
-      *reinterpret_cast<int4*>(lmap + 4 * pos) = int4{e, off + nfull * BM, rem, 0};
+      *reinterpret_cast<int4*>(lmap + 4 * pos) = int4{e, off + nfull * LR, rem, 0};
     }
     if (e == MOE_MAX_EXPERTS - 1 && has_shared) {
       const int R = bc + ic;  // total routed rows: the last thread's inclusive scan
       for (int i = 0; i < sfull; ++i)
-        *reinterpret_cast<int4*>(lmap + 4 * (ftot + i)) = int4{E, R + i * LR, min(LR, T - i * LR), 0};
-      if (srem > 0) *reinterpret_cast<int4*>(lmap + 4 * (st_s + nb_s)) = int4{E, R + sfull * BM, srem, 0};
+        *reinterpret_cast<int4*>(lmap + 4 * (ftot + i)) = int4{E, R + i * LR, LR, 0};
+      if (srem > 0) *reinterpret_cast<int4*>(lmap + 4 * (st_s + nb_s)) = int4{E, R + sfull * LR, srem, 0};
     }
   }
   // ---- scatter of this group's rows -------------------------------------------
