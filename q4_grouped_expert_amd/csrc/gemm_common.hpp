@@ -16,19 +16,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 }
 
 // 8 codes (element 2i in the low nibble of byte i, 2i+1 in the high) ->
-// bf16(fma(q, s, b)) for each, in element order.  The nibble masks are
-// applied in asm so the compiler converts bytes with v_cvt_f32_ubyte{0..3}.
+// bf16(fma(q, s, b)) for each, in element order.  After the nibble masks
+// every byte holds one code q in its low four bits; read as an fp8 E4M3 byte
+// that is q * 2^-9 exactly (codes 0..7 are the subnormals m * 2^-9, codes
+// 8..15 the first normal binade (1 + m/8) * 2^-6), so the packed fp8
+// conversion with scale 2^9 turns two bytes into two exact float codes per
+// instruction.  The masks are applied in asm so the compiler keeps them.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
   uint32_t lo, hi;
   asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
   asm("v_lshrrev_b32 %0, 4, %1\n\tv_and_b32 %0, 0x0f0f0f0f, %0" : "=&v"(hi) : "v"(d));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 e02 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);  // elements 0, 2
+  const f32x2 e46 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);   // elements 4, 6
+  const f32x2 e13 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);  // elements 1, 3
+  const f32x2 e57 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);   // elements 5, 7
   u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float q0 = (float)((lo >> (8 * i)) & 0xFFu);
-    const float q1 = (float)((hi >> (8 * i)) & 0xFFu);
-    r[i] = pack_bf16x2(__builtin_fmaf(q0, s, b), __builtin_fmaf(q1, s, b));
-  }
+  r[0] = pack_bf16x2(__builtin_fmaf(e02[0], s, b), __builtin_fmaf(e13[0], s, b));
+  r[1] = pack_bf16x2(__builtin_fmaf(e02[1], s, b), __builtin_fmaf(e13[1], s, b));
+  r[2] = pack_bf16x2(__builtin_fmaf(e46[0], s, b), __builtin_fmaf(e57[0], s, b));
+  r[3] = pack_bf16x2(__builtin_fmaf(e46[1], s, b), __builtin_fmaf(e57[1], s, b));
   return __builtin_bit_cast(bf16x8, r);
 }
 

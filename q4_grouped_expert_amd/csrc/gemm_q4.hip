@@ -27,12 +27,13 @@
 //    reads conflict-free.
 //  * Weights go from global memory straight to VGPRs through buffer loads
 //    (per-lane row offset in a VGPR, stage offset in an SGPR), two stages
-//    ahead of use: a lane loads 8 bytes = 16 codes of one weight row, forms
-//    q*scale+bias with one fma per weight in fp32, rounds to bf16 and feeds
-//    the result as the A operand of v_mfma_f32_16x16x32_bf16 (activations
-//    are the B operand, so each lane ends with 4 consecutive output columns
-//    of one row); accumulation is fp32.  The tile's scales and biases for the
-//    whole reduction are loaded once per tile into LDS tables.
+//    ahead of use: a lane loads 8 bytes = 16 codes of one weight row, turns
+//    codes into floats two at a time (packed fp8 conversion of the masked
+//    nibbles), forms q*scale+bias with one fma per weight in fp32, rounds to
+//    bf16 and feeds the result as the A operand of v_mfma_f32_16x16x32_bf16
+//    (activations are the B operand, so each lane ends with 4 consecutive
+//    output columns of one row); accumulation is fp32.  The tile's scales and
+//    biases for the whole reduction are loaded once per tile into LDS tables.
 //  * Tiles of at most 4 row subtiles (64 rows) have too little matrix work
 //    per stage to cover memory latency with that pipeline; they run a 4-slot
 //    LDS ring that holds both the activations and the codes of a stage, each
