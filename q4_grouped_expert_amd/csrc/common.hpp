@@ -55,8 +55,8 @@ struct RouteArgs {
   // null, or where the grouping also lists the GEMMs' tiles in launch order
   // (n_launch entries): launch_rows == kTileRows: the block map's tiles, most
   // 16-row subtiles first; launch_rows == kSmallRows: every expert's rows in
-  // pieces of at most kSmallRows rows, in expert order, the shared expert's
-  // last
+  // pieces of at most kSmallRows rows, in the same order (full pieces first,
+  // then the partial ones by subtile count)
   int32_t* launch_map;
   int32_t* n_launch;
   int launch_rows;

@@ -866,6 +866,7 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void route_group_kernel(const int3
     }
   }
   // ---- launch order, part 2: every tile's place, stored with the block map ----
+  // (with pieces, a full tile is a full piece of LR rows)
   // bucket 0 (16 subtiles): the experts' full tiles in expert order, the
   // shared expert's full tiles, then the partial tiles of 16 subtiles;
   // buckets 1.. : partial tiles in expert order, the shared expert's last
