@@ -477,7 +477,9 @@ constexpr int kSmallQElems = kRingW + NWAVES * 512;
 
 // kRing: slots (4: loads three stages ahead; the small-prompt kernel's 3: two
 // stages ahead, in less LDS)
-template <bool kGateUp, int MSUB, int kRing, int QE>
+// kTbl: the kernel instance's table capacity (only tells instances apart: the
+// host compile pass accepts a body instance from one kernel instance only)
+template <bool kGateUp, int MSUB, int kRing, int QE, int kTbl>
 __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx& t, const LdsQ& L,
                                                uint16_t* __restrict__ Ssh, uint16_t* __restrict__ Bsh) {
   static_assert(kRing == 3 || kRing == 4, "ring slots");
@@ -608,8 +610,11 @@ __device__ __forceinline__ void tile_body_ring(const GemmArgs& g, const TileCtx&
 // kSmall: the small-prompt kernel, over a list of pieces of at most
 // kSmallRows rows, all in the short-tile form with a 3-slot ring: 52 KB of
 // LDS (gate/up) and three workgroups per CU instead of two.
-template <bool kGateUp, bool kBf16W, bool kSmall>
-__global__ __launch_bounds__(NT, kSmall ? 3 : 2) void gemm_q4_kernel(GemmArgs g) {
+// kTblGroups: quant groups per weight row the LDS tables hold; the small
+// kernel's down GEMM with at most 8 (a reduction of at most 512) keeps 40 KB of
+// LDS and four workgroups per CU.
+template <bool kGateUp, bool kBf16W, bool kSmall, int kTblGroups>
+__global__ __launch_bounds__(NT, kSmall ? (kTblGroups <= 8 ? 4 : 3) : 2) void gemm_q4_kernel(GemmArgs g) {
   // activation ring: two stages of [256 rows][64] bf16, as four arrays of
   // 128 rows (short tiles: a 4-slot ring of activations and codes); the
   // small kernel: three arrays of one 3-slot ring's slot each
@@ -620,8 +625,8 @@ __global__ __launch_bounds__(NT, kSmall ? 3 : 2) void gemm_q4_kernel(GemmArgs g)
   __shared__ __attribute__((aligned(16))) uint16_t Lq3[kSmall ? 8 : kQElems];  // not used by the small kernel
   const LdsQ L{Lq0, Lq1, Lq2, kSmall ? Lq2 : Lq3};
   // the tile's scales and biases: [128 weight rows][<= 32 groups] bf16 each
-  __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kMaxGroups];
-  __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kMaxGroups];
+  __shared__ __attribute__((aligned(16))) uint16_t Ssh[BN * kTblGroups];
+  __shared__ __attribute__((aligned(16))) uint16_t Bsh[BN * kTblGroups];
 
   // ---- which tile / column slice -------------------------------------------
   const int nN = kGateUp ? (g.I + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
@@ -742,29 +747,29 @@ __global__ __launch_bounds__(NT, kSmall ? 3 : 2) void gemm_q4_kernel(GemmArgs g)
   if constexpr (kSmall) {
     static_assert(!kBf16W && kSmallRows == 16 * kRingMaxSub, "the small kernel runs 4-bit pieces of the ring form");
     switch (msub) {
-      case 1: tile_body_ring<kGateUp, 1, 3, QE>(g, t, L, Ssh, Bsh); break;
-      case 2: tile_body_ring<kGateUp, 2, 3, QE>(g, t, L, Ssh, Bsh); break;
-      case 3: tile_body_ring<kGateUp, 3, 3, QE>(g, t, L, Ssh, Bsh); break;
-      default: tile_body_ring<kGateUp, 4, 3, QE>(g, t, L, Ssh, Bsh); break;
+      case 1: tile_body_ring<kGateUp, 1, 3, QE, kTblGroups>(g, t, L, Ssh, Bsh); break;
+      case 2: tile_body_ring<kGateUp, 2, 3, QE, kTblGroups>(g, t, L, Ssh, Bsh); break;
+      case 3: tile_body_ring<kGateUp, 3, 3, QE, kTblGroups>(g, t, L, Ssh, Bsh); break;
+      default: tile_body_ring<kGateUp, 4, 3, QE, kTblGroups>(g, t, L, Ssh, Bsh); break;
     }
   } else {
     // (not instantiated in the small kernel, so no tile-body instance is
     // shared by two kernel instances)
     switch (msub) {
       case 1:
-        if constexpr (!kBf16W) tile_body_ring<kGateUp, 1, 4, QE>(g, t, L, Ssh, Bsh);
+        if constexpr (!kBf16W) tile_body_ring<kGateUp, 1, 4, QE, kTblGroups>(g, t, L, Ssh, Bsh);
         else tile_body<kGateUp, kBf16W, 1>(g, t, L, Ssh, Bsh);
         break;
       case 2:
-        if constexpr (!kBf16W && kRingMaxSub >= 2) tile_body_ring<kGateUp, 2, 4, QE>(g, t, L, Ssh, Bsh);
+        if constexpr (!kBf16W && kRingMaxSub >= 2) tile_body_ring<kGateUp, 2, 4, QE, kTblGroups>(g, t, L, Ssh, Bsh);
         else tile_body<kGateUp, kBf16W, 2>(g, t, L, Ssh, Bsh);
         break;
       case 3:
-        if constexpr (!kBf16W && kRingMaxSub >= 3) tile_body_ring<kGateUp, 3, 4, QE>(g, t, L, Ssh, Bsh);
+        if constexpr (!kBf16W && kRingMaxSub >= 3) tile_body_ring<kGateUp, 3, 4, QE, kTblGroups>(g, t, L, Ssh, Bsh);
         else tile_body<kGateUp, kBf16W, 3>(g, t, L, Ssh, Bsh);
         break;
       case 4:
-        if constexpr (!kBf16W && kRingMaxSub >= 4) tile_body_ring<kGateUp, 4, 4, QE>(g, t, L, Ssh, Bsh);
+        if constexpr (!kBf16W && kRingMaxSub >= 4) tile_body_ring<kGateUp, 4, 4, QE, kTblGroups>(g, t, L, Ssh, Bsh);
         else tile_body<kGateUp, kBf16W, 4>(g, t, L, Ssh, Bsh);
         break;
       case 5: tile_body<kGateUp, kBf16W, 5>(g, t, L, Ssh, Bsh); break;
@@ -790,18 +795,22 @@ int grid_blocks(int max_tiles, int nN) { return (max_tiles + kXcds - 1) / kXcds 
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.N + BN - 1) / BN;
   const dim3 grid(grid_blocks(g.max_tiles, nN));
-  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<false, true, false>), grid, dim3(NT), 0, stream, g);
-  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<false, false, true>), grid, dim3(NT), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_q4_kernel<false, false, false>), grid, dim3(NT), 0, stream, g);
+  constexpr int G = kMaxGroups;
+  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<false, true, false, G>), grid, dim3(NT), 0, stream, g);
+  else if (g.small && g.Kdim <= 8 * 64)
+    hipLaunchKernelGGL((gemm_q4_kernel<false, false, true, 8>), grid, dim3(NT), 0, stream, g);
+  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<false, false, true, G>), grid, dim3(NT), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_q4_kernel<false, false, false, G>), grid, dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t stream) {
   const int nN = (g.I + BN / 2 - 1) / (BN / 2);
   const dim3 grid(grid_blocks(g.max_tiles, nN));
-  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<true, true, false>), grid, dim3(NT), 0, stream, g);
-  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<true, false, true>), grid, dim3(NT), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_q4_kernel<true, false, false>), grid, dim3(NT), 0, stream, g);
+  constexpr int G = kMaxGroups;
+  if (g.wbf) hipLaunchKernelGGL((gemm_q4_kernel<true, true, false, G>), grid, dim3(NT), 0, stream, g);
+  else if (g.small) hipLaunchKernelGGL((gemm_q4_kernel<true, false, true, G>), grid, dim3(NT), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_q4_kernel<true, false, false, G>), grid, dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
